@@ -1,0 +1,195 @@
+"""Reducer state machine and bucket reduction (oracle).
+
+R data-parallel replicas are held side by side: ``grads[r][v]`` is replica r's
+gradient of variable v, a 1-D float32 NumPy array that the reducer updates in
+place, as the real reducer writes the averaged values back into every
+parameter's ``.grad``.
+
+Steps, in the pages' order:
+
+* per-bucket state: a pending count equal to the number of member variables
+  ([Li] "Overlapping Computation with Communication", per-hook logic;
+  [C30] "Variable 到 Bucket");
+* ``mark_ready(v)``: copy v's gradient into its narrowed view of the flat
+  bucket, decrement pending; when it reaches zero the bucket is ready
+  ([Li] same subsection; [PDTI] §2);
+* ready buckets are launched strictly in bucket-index order; a bucket that
+  becomes ready before its predecessors were launched waits (is parked) and is
+  launched as soon as every earlier bucket has been ([Li] "Launching AllReduce
+  in order"; [C30] "Bucket 必须按序发起");
+* a launched bucket is averaged over the replicas and the result is written
+  back to each member's gradient on every replica ([TP] "Internal Design",
+  backward pass; [PDTI] §3; [Li] "After AllReduce: writing averaged gradients
+  back");
+* ``finalize()`` at the end of backward requires every bucket to have been
+  launched; otherwise the reduction is incomplete and the next iteration fails
+  ([TP] "When a parameter never receives a gradient"; [C30] "未检测的失败");
+* ``no_sync``: while synchronisation is off the hooks do nothing and gradients
+  accumulate additively across backward passes ([Li] "Gradient Accumulation
+  (no_sync)"; [TP] "Gradient sync you can turn off").
+
+Readings of points the pages leave open:
+* the average is the sum over replicas 0..R-1 taken left to right in float32
+  (acc = g_0, then acc + g_1, ...), followed by one IEEE division by R
+  (round to nearest even, subnormals kept). For float32 the pages say the
+  bucket is averaged directly; dividing first and summing after would give the
+  same bits for power-of-two R in the absence of underflow, but not in general;
+* copy-back happens per bucket right after its reduction; ``finalize`` only
+  checks completeness and resets the per-iteration state;
+* all R replicas run their hooks in lockstep: one ``mark_ready(v)`` means v's
+  gradient is final on every replica;
+* marking the same variable twice in one iteration is an error.
+"""
+from __future__ import annotations
+
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+from .plan import compute_bucket_assignment_by_size, locators, bucket_numels
+
+
+class ReductionIncomplete(RuntimeError):
+    """The prior iteration did not finish reducing every bucket."""
+
+
+class DoubleReady(RuntimeError):
+    """A variable was marked ready twice in one iteration."""
+
+
+def fixed_order_mean(bufs: Sequence[np.ndarray]) -> np.ndarray:
+    """m = fl(fl(... fl(g_0 + g_1) ... + g_{R-1}) / R), elementwise, float32."""
+    R = len(bufs)
+    if R < 1:
+        raise ValueError("need at least one replica")
+    acc = np.array(bufs[0], dtype=np.float32, copy=True)
+    for r in range(1, R):
+        acc = acc + np.asarray(bufs[r], dtype=np.float32)
+    return acc / np.float32(R)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen bf16 (given as uint16 bit patterns) to float32 exactly: a bf16
+    value is the upper half of the binary32 encoding."""
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+class Reducer:
+    def __init__(self, numels: Sequence[int], R: int, bucket_cap_bytes: int,
+                 elem_size: int = 4):
+        if R < 1:
+            raise ValueError("R must be >= 1")
+        self.numels = [int(n) for n in numels]
+        self.P = len(self.numels)
+        self.R = R
+        self.buckets = compute_bucket_assignment_by_size(self.numels, elem_size, bucket_cap_bytes)
+        self.loc = locators(self.buckets, self.numels)
+        self.B = len(self.buckets)
+        self.bucket_elems = bucket_numels(self.buckets, self.numels)
+        self.sync_enabled = True
+        self.failed = False
+        self.grads: Optional[List[List[np.ndarray]]] = None
+        # per-replica flat buckets (the pages' flat bucket buffers)
+        self.flat = [[np.zeros(n, dtype=np.float32) for n in self.bucket_elems] for _ in range(R)]
+        self.averaged = [np.zeros(n, dtype=np.float32) for n in self.bucket_elems]
+        self.launch_log: List[Tuple[int, int]] = []   # (bucket, index of triggering mark_ready call)
+        self._reset_iteration()
+
+    # -- state ---------------------------------------------------------------
+    def _reset_iteration(self):
+        self.pending = [len(m) for m in self.buckets]
+        self.ready = [False] * self.P
+        self.next_bucket = 0
+        self.calls = 0
+
+    def bind(self, grads: List[List[np.ndarray]]):
+        if len(grads) != self.R or any(len(row) != self.P for row in grads):
+            raise ValueError("grads must be R x P")
+        for row in grads:
+            for v, g in enumerate(row):
+                if g.dtype != np.float32 or g.ndim != 1 or g.size != self.numels[v]:
+                    raise ValueError(f"grad {v}: need flat float32 of {self.numels[v]} elements")
+        self.grads = grads
+
+    def set_sync(self, enabled: bool):
+        if self.calls:
+            raise RuntimeError("cannot toggle sync in the middle of an iteration")
+        self.sync_enabled = bool(enabled)
+
+    def ensure_prior_reduction_finished(self):
+        if self.failed or self.calls:
+            self.failed = True
+            raise ReductionIncomplete(
+                "prior iteration did not finish reducing every bucket")
+
+    # -- hooks ---------------------------------------------------------------
+    def mark_ready(self, v: int):
+        if not self.sync_enabled:
+            return
+        if self.failed:
+            raise ReductionIncomplete("prior iteration did not finish reducing every bucket")
+        if not (0 <= v < self.P):
+            raise IndexError(v)
+        if self.ready[v]:
+            raise DoubleReady(v)
+        self.ready[v] = True
+        call = self.calls
+        self.calls += 1
+        L = self.loc[v]
+        for r in range(self.R):          # the view copy: bucket.narrow(offset, numel) <- grad
+            self.flat[r][L.bucket][L.offset:L.offset + L.length] = self.grads[r][v]
+        self.pending[L.bucket] -= 1
+        if self.pending[L.bucket] == 0:
+            self._mark_bucket_ready(L.bucket, call)
+
+    def _mark_bucket_ready(self, b: int, call: int):
+        if b > self.next_bucket:
+            return                        # parked until every earlier bucket launched
+        while self.next_bucket < self.B and self.pending[self.next_bucket] == 0:
+            self._launch(self.next_bucket, call)
+            self.next_bucket += 1
+
+    def _launch(self, b: int, call: int):
+        m = fixed_order_mean([self.flat[r][b] for r in range(self.R)])
+        self.averaged[b] = m
+        for v in self.buckets[b]:
+            L = self.loc[v]
+            for r in range(self.R):
+                self.grads[r][v][...] = m[L.offset:L.offset + L.length]
+        self.launch_log.append((b, call))
+
+    def finalize(self):
+        if not self.sync_enabled and self.calls == 0:
+            return
+        if self.next_bucket != self.B:
+            self.failed = True
+            raise ReductionIncomplete(
+                f"only {self.next_bucket} of {self.B} buckets were reduced")
+        self._reset_iteration()
+
+    def reset(self):
+        self.failed = False
+        self._reset_iteration()
+
+    # -- no_sync -------------------------------------------------------------
+    def no_sync_accumulate(self, step: List[List[np.ndarray]], first: bool):
+        """One local backward's contribution: ``grad = step`` on the first
+        micro-step, ``grad += step`` afterwards (float32). ``step`` holds
+        float32 arrays, or uint16 arrays of bf16 bit patterns."""
+        for r in range(self.R):
+            for v in range(self.P):
+                s = step[r][v]
+                s32 = bf16_bits_to_f32(s) if s.dtype == np.uint16 else np.asarray(s, dtype=np.float32)
+                if first:
+                    self.grads[r][v][...] = s32
+                else:
+                    self.grads[r][v][...] = self.grads[r][v] + s32
+
+    # -- one whole synchronisation -------------------------------------------
+    def sync(self, order: Optional[Sequence[int]] = None):
+        """Run every hook in ``order`` (default: reverse index) and finalize."""
+        if order is None:
+            order = range(self.P - 1, -1, -1)
+        for v in order:
+            self.mark_ready(v)
+        self.finalize()
