@@ -1,0 +1,206 @@
+// core.cpp -- bucket plan, segment table and readiness state machine.
+// Page citations use the short names defined in core.hpp.
+#include "core.hpp"
+
+#include <algorithm>
+#include <utility>
+
+namespace ddpb {
+
+static int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+Plan make_plan(const std::vector<int64_t>& numel, int64_t elem_size, int64_t cap_bytes, int32_t R) {
+  Plan p;
+  p.P = static_cast<int32_t>(numel.size());
+  p.R = R;
+  p.cap_bytes = cap_bytes;
+  p.elem_size = elem_size;
+  p.numel = numel;
+
+  // [Li] "Gradient Bucketing" / [C30] "bucket_cap_mb 不是张量切分器": walk the
+  // parameters last to first, add each whole tensor, close the bucket once its
+  // size reaches or exceeds the cap; the last, partly filled bucket is kept.
+  std::vector<int32_t> cur;
+  int64_t size = 0;
+  for (int32_t v = p.P - 1; v >= 0; --v) {
+    cur.push_back(v);
+    size += numel[v] * elem_size;
+    if (size >= cap_bytes) {
+      p.members.push_back(std::move(cur));
+      cur.clear();
+      size = 0;
+    }
+  }
+  if (!cur.empty()) p.members.push_back(std::move(cur));
+
+  // [C30] "Variable 到 Bucket": variable -> (bucket, intra-bucket index,
+  // offset, length); members sit back to back in insertion order.
+  const int32_t B = p.B();
+  p.loc.assign(p.P, Locator{-1, -1, 0, 0});
+  p.bucket_elems.assign(B, 0);
+  p.flat_base.assign(B, 0);
+  int64_t base = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    int64_t off = 0;
+    for (size_t i = 0; i < p.members[b].size(); ++i) {
+      const int32_t v = p.members[b][i];
+      p.loc[v] = Locator{b, static_cast<int32_t>(i), off, numel[v]};
+      off += numel[v];
+    }
+    p.bucket_elems[b] = off;
+    p.flat_base[b] = base;
+    base += round_up(off, kFlatAlignElems);
+  }
+  p.flat_elems = base;
+
+  // Device work table: every member cut into segments of <= kSegElems.
+  p.seg_first.assign(B + 1, 0);
+  for (int32_t b = 0; b < B; ++b) {
+    p.seg_first[b] = static_cast<int32_t>(p.segs.size());
+    for (int32_t v : p.members[b]) {
+      const Locator& L = p.loc[v];
+      for (int64_t s = 0; s < numel[v]; s += kSegElems) {
+        Segment g;
+        g.var = v;
+        g.start = s;
+        g.len = std::min(kSegElems, numel[v] - s);
+        g.boff = L.offset + s;
+        g.flags = (g.start % 4 == 0 ? kSegVecStart : 0) | (g.boff % 4 == 0 ? kSegVecFlat : 0);
+        p.segs.push_back(g);
+        p.seg_bucket.push_back(b);
+      }
+    }
+  }
+  p.seg_first[B] = static_cast<int32_t>(p.segs.size());
+  return p;
+}
+
+int64_t workspace_bytes(const Plan& plan, int32_t mode) {
+  if (mode == 1) return (static_cast<int64_t>(plan.R) + 1) * plan.flat_elems * plan.elem_size;
+  return 0;
+}
+
+Reducer::Reducer(Plan plan) : plan_(std::move(plan)), launcher_(make_launcher()) {
+  begin_iteration();
+}
+
+void Reducer::begin_iteration() {
+  const int32_t B = plan_.B();
+  pending_.resize(B);
+  for (int32_t b = 0; b < B; ++b) pending_[b] = static_cast<int32_t>(plan_.members[b].size());
+  ready_.assign(plan_.P, 0);
+  next_bucket_ = 0;
+  calls_ = 0;
+}
+
+int Reducer::bind(const BindArgs& args, std::string* err) {
+  if (iteration_open()) {
+    *err = "bind: an iteration is in progress";
+    return kErrState;
+  }
+  const int rc = launcher_->bind(plan_, args, err);
+  bound_ = (rc == kOk);
+  return rc;
+}
+
+// [TP] "When a parameter never receives a gradient": the failure of an
+// iteration that never finished reducing shows up at the next forward.
+int Reducer::ensure_prior_reduction_finished(std::string* err) {
+  if (failed_ || iteration_open()) {
+    failed_ = true;
+    *err = "Expected to have finished reduction in the prior iteration before starting a new one";
+    return kErrIncomplete;
+  }
+  return kOk;
+}
+
+int Reducer::mark_ready(int32_t v, std::string* err) {
+  if (!bound_) {
+    *err = "mark_ready: reducer is not bound";
+    return kErrState;
+  }
+  if (v < 0 || v >= plan_.P) {
+    *err = "mark_ready: variable index out of range";
+    return kErrIndex;
+  }
+  if (!sync_) return kOk;     // no_sync: the hook runs but does nothing
+  if (failed_) {
+    *err = "Expected to have finished reduction in the prior iteration before starting a new one";
+    return kErrIncomplete;
+  }
+  if (ready_[v]) {
+    *err = "mark_ready: variable marked ready twice in one iteration";
+    return kErrDoubleReady;
+  }
+  if (calls_ == 0) log_.clear();
+  ready_[v] = 1;
+  const int32_t call = calls_++;
+  const int32_t b = plan_.loc[v].bucket;
+  // [Li] per-hook logic: decrement the bucket's pending count; at zero the
+  // bucket is ready. [C30] "Bucket 必须按序发起": only the bucket at
+  // next_bucket_ may launch, followed by every already complete successor; a
+  // later bucket that completes first stays parked.
+  if (--pending_[b] == 0 && b == next_bucket_) {
+    const int32_t first = next_bucket_;
+    while (next_bucket_ < plan_.B() && pending_[next_bucket_] == 0) {
+      log_.push_back(LaunchRecord{next_bucket_, call});
+      ++next_bucket_;
+    }
+    const int rc = launcher_->launch(first, next_bucket_ - 1, finalized_, err);
+    if (rc != kOk) {
+      failed_ = true;
+      return rc;
+    }
+  }
+  return kOk;
+}
+
+int Reducer::finalize(std::string* err) {
+  if (!bound_) {
+    *err = "finalize: reducer is not bound";
+    return kErrState;
+  }
+  if (!sync_ && calls_ == 0) return kOk;
+  if (failed_ || next_bucket_ != plan_.B()) {
+    failed_ = true;
+    *err = "finalize: not every bucket was reduced in this iteration (" +
+           std::to_string(next_bucket_) + " of " + std::to_string(plan_.B()) + " launched)";
+    return kErrIncomplete;
+  }
+  // [C30] "Finalize Backward 与梯度可见性": the compute stream is ordered after
+  // every bucket's reduction, without a host synchronization.
+  const int rc = launcher_->join(err);
+  log_ring_[finalized_ % kTimeRing] = log_;
+  ++finalized_;
+  begin_iteration();
+  return rc;
+}
+
+int Reducer::set_sync(bool enabled, std::string* err) {
+  if (iteration_open()) {
+    *err = "set_sync: an iteration is in progress";
+    return kErrState;
+  }
+  sync_ = enabled;
+  return kOk;
+}
+
+int Reducer::accumulate(void* const* step_ptrs, int32_t step_dtype, bool first, std::string* err) {
+  if (!bound_) {
+    *err = "no_sync_accumulate: reducer is not bound";
+    return kErrState;
+  }
+  if (step_ptrs == nullptr || (step_dtype != 0 && step_dtype != 1)) {
+    *err = "no_sync_accumulate: bad step pointers or dtype";
+    return kErrArg;
+  }
+  return launcher_->accumulate(step_ptrs, step_dtype, first, err);
+}
+
+int Reducer::reset() {
+  failed_ = false;
+  begin_iteration();
+  return kOk;
+}
+
+}  // namespace ddpb

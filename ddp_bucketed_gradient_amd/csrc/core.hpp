@@ -1,0 +1,157 @@
+// core.hpp -- host side of the bucketed gradient reducer: bucket plan,
+// variable locator, device work (segment) table and the readiness state
+// machine. No HIP types appear here; device work goes through Launcher.
+//
+// Pages cited (titles shortened):
+//   [Li]  "PyTorch Distributed: Experiences on Accelerating Data Parallel
+//         Training" summary, §3.4 "Gradient Bucketing", "Overlapping
+//         Computation with Communication", "Gradient Accumulation (no_sync)".
+//   [TP]  tensorplay "Distributed Data Parallel" notes, "Internal Design",
+//         "When a parameter never receives a gradient".
+//   [C30] "NCCL 专家课程 30" blog, "Variable 到 Bucket", "Bucket 必须按序发起",
+//         "bucket_cap_mb 不是张量切分器", "Finalize Backward 与梯度可见性".
+#pragma once
+
+#include <cstdint>
+#include <memory>
+#include <string>
+#include <vector>
+
+namespace ddpb {
+
+// Elements per device segment: one wavefront processes one segment.
+constexpr int64_t kSegElems = 4096;
+// Flat-bucket bases in the staged workspace are padded to this many elements.
+constexpr int64_t kFlatAlignElems = 64;
+constexpr int kMaxReplicas = 64;
+// Launch-timing events are kept for this many most recent iterations.
+constexpr int kTimeRing = 4;
+
+enum Status : int {
+  kOk = 0, kErrArg = -1, kErrIndex = -2, kErrDoubleReady = -3,
+  kErrIncomplete = -4, kErrState = -5, kErrHip = -6, kErrNoMem = -7
+};
+
+// Device-side work descriptor, 32 bytes, read by the kernels.
+struct Segment {
+  int32_t var;        // variable index
+  int32_t flags;      // kSegVec* bits: which float4 accesses are legal
+  int64_t start;      // first element inside the variable
+  int64_t len;        // number of elements
+  int64_t boff;       // element offset inside the flat bucket
+};
+static_assert(sizeof(Segment) == 32, "segment layout is shared with the kernels");
+constexpr int32_t kSegVecStart = 1;   // start is a multiple of 4 elements
+constexpr int32_t kSegVecFlat = 2;    // boff is a multiple of 4 elements
+constexpr int32_t kSegVecBoth = kSegVecStart | kSegVecFlat;
+
+struct Locator {
+  int32_t bucket;
+  int32_t intra;
+  int64_t offset;
+  int64_t length;
+};
+
+struct Plan {
+  int32_t P = 0;
+  int32_t R = 0;
+  int64_t cap_bytes = 0;
+  int64_t elem_size = 4;
+  std::vector<int64_t> numel;                  // per variable
+  std::vector<std::vector<int32_t>> members;   // per bucket, in bucket order
+  std::vector<int64_t> bucket_elems;           // per bucket
+  std::vector<int64_t> flat_base;              // per bucket, padded element base in a flat buffer
+  int64_t flat_elems = 0;                      // padded total (one replica)
+  std::vector<Locator> loc;                    // per variable
+  std::vector<Segment> segs;                   // bucket by bucket
+  std::vector<int32_t> seg_first;              // per bucket, size B + 1
+  std::vector<int32_t> seg_bucket;             // per segment
+
+  int32_t B() const { return static_cast<int32_t>(members.size()); }
+};
+
+// Reverse-order greedy assignment under the cap ([Li] "Gradient Bucketing";
+// [C30] "bucket_cap_mb 不是张量切分器"), then locators, flat bases and segments.
+Plan make_plan(const std::vector<int64_t>& numel, int64_t elem_size, int64_t cap_bytes, int32_t R);
+
+struct BindArgs {
+  std::vector<void*> grad_ptrs;     // R * P, replica-major
+  void* workspace = nullptr;
+  int64_t ws_bytes = 0;
+  void* compute_stream = nullptr;
+  std::vector<void*> side_streams;
+  int32_t mode = 0;
+  int32_t flags = 0;
+};
+
+int64_t workspace_bytes(const Plan& plan, int32_t mode);
+
+struct LaunchRecord {
+  int32_t bucket;
+  int32_t trigger_call;
+};
+
+// Device work. The HIP implementation enqueues kernels; the test build only
+// records what would be enqueued.
+class Launcher {
+ public:
+  virtual ~Launcher() = default;
+  virtual int bind(const Plan& plan, const BindArgs& args, std::string* err) = 0;
+  // Buckets [first, last] are complete and every earlier bucket has been
+  // launched: order them after the compute stream's current work and enqueue
+  // their reduction on the side stream(s), in index order.
+  // `iteration` counts finalized iterations before this one.
+  virtual int launch(int32_t first, int32_t last, int64_t iteration, std::string* err) = 0;
+  // End of iteration: the compute stream waits for every side stream.
+  virtual int join(std::string* err) = 0;
+  virtual int accumulate(void* const* step_ptrs, int32_t step_dtype, bool first, std::string* err) = 0;
+  // Device clock stamps of the given launched buckets (zeros when disabled).
+  virtual int read_stamps(const std::vector<LaunchRecord>& log, std::vector<int64_t>* t0,
+                          std::vector<int64_t>* t1, std::string* err) = 0;
+  // Waits for, then returns, the kernel time of each launch of `iteration`.
+  virtual int read_times(int64_t iteration, const std::vector<LaunchRecord>& log, std::vector<float>* ms,
+                         std::string* err) = 0;
+  virtual int clock_hz(int64_t* hz, std::string* err) = 0;
+};
+
+std::unique_ptr<Launcher> make_launcher();
+
+// The readiness state machine ([Li] per-hook logic and "Launching AllReduce in
+// order"; [C30] "Variable 到 Bucket", "Bucket 必须按序发起").
+class Reducer {
+ public:
+  explicit Reducer(Plan plan);
+  const Plan& plan() const { return plan_; }
+
+  int bind(const BindArgs& args, std::string* err);
+  int ensure_prior_reduction_finished(std::string* err);
+  int mark_ready(int32_t v, std::string* err);
+  int finalize(std::string* err);
+  int set_sync(bool enabled, std::string* err);
+  int accumulate(void* const* step_ptrs, int32_t step_dtype, bool first, std::string* err);
+  int reset();
+  const std::vector<LaunchRecord>& log() const { return log_; }
+  int64_t finalized() const { return finalized_; }
+  // Launches of finalized iteration `it` (only the last kTimeRing are kept).
+  const std::vector<LaunchRecord>& log_of(int64_t it) const { return log_ring_[it % kTimeRing]; }
+  Launcher* launcher() { return launcher_.get(); }
+
+ private:
+  void begin_iteration();
+  bool iteration_open() const { return calls_ > 0; }
+
+  Plan plan_;
+  std::unique_ptr<Launcher> launcher_;
+  bool bound_ = false;
+  bool sync_ = true;
+  bool failed_ = false;            // latched "prior reduction did not finish"
+  std::vector<int32_t> pending_;   // per bucket
+  std::vector<uint8_t> ready_;     // per variable
+  int32_t next_bucket_ = 0;
+  int32_t calls_ = 0;              // mark_ready calls that counted, this iteration
+  std::vector<LaunchRecord> log_;
+  int64_t finalized_ = 0;          // iterations finalized so far
+  std::vector<LaunchRecord> log_ring_[kTimeRing];
+};
+
+}  // namespace ddpb

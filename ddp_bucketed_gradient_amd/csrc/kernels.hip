@@ -1,0 +1,711 @@
+// kernels.hip -- CDNA4 (gfx950) kernels and the HIP launcher of the bucketed
+// gradient reducer.
+//
+// The reduction of one bucket ([Li] "Overlapping Computation with
+// Communication"; [TP] "Internal Design", backward pass; [PDTI] §3) is the
+// elementwise mean over R replicas, m = fl(fl(..fl(g_0 + g_1).. + g_{R-1}) / R),
+// summed in replica order in fp32 and divided once (IEEE, nearest-even),
+// written back into every replica's gradient. On one GPU the replicas sit in
+// HBM, so the path is bound by HBM bandwidth: each kernel streams its bytes
+// once with 128-bit accesses and does a handful of adds per element.
+//
+// Work decomposition: the host cuts every bucket member into segments of at
+// most 4096 elements (core.cpp). One wavefront owns one segment; a workgroup
+// of 256 threads owns four consecutive segments. Each lane moves v4fs at
+// lane stride, so one instruction covers 1 KiB of contiguous memory per
+// replica, and it issues all R (x unroll) loads before the first add to keep
+// enough bytes in flight.
+//
+// Kernels
+//   fused_mean_kernel   gather (pack), R-way mean and copy-back in one pass:
+//                       reads R*S_b and writes R*S_b bytes per bucket.
+//   pack_kernel         staged step 1: R gradients -> R flat buckets.
+//   mean_kernel         staged step 2: R flat buckets -> averaged bucket,
+//                       grid-stride over contiguous v4fs.
+//   copyback_kernel     staged step 3: averaged bucket -> R gradients.
+//   accumulate_kernel   no_sync: grad (+)= float(step) for every replica.
+//
+// Short page names are defined in core.hpp.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <vector>
+
+#include "core.hpp"
+
+namespace ddpb {
+namespace {
+
+constexpr int kWavesPerBlock = 4;
+constexpr int kBlock = 64 * kWavesPerBlock;
+constexpr int kStepSlots = 8;
+
+#define HIP_OK(expr, what)                                                        \
+  do {                                                                            \
+    hipError_t e_ = (expr);                                                       \
+    if (e_ != hipSuccess) {                                                       \
+      *err = std::string(what) + ": " + hipGetErrorString(e_);                    \
+      return kErrHip;                                                             \
+    }                                                                             \
+  } while (0)
+
+// ---------------------------------------------------------------------------
+// device helpers
+
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Gradient pointers come from a device table, so the compiler cannot tell
+// they address global memory and would emit flat accesses (which share a
+// counter with scalar loads and force full waits). All gradient traffic goes
+// through address-space-1 pointers to native 4-wide vectors instead, which
+// become global_load_dwordx4 / global_store_dwordx4.
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) float gfloat;
+typedef __attribute__((address_space(1))) v4f gv4f;
+
+__device__ __forceinline__ gfloat* G(float* p) { return (gfloat*)p; }
+__device__ __forceinline__ const gfloat* G(const float* p) { return (const gfloat*)p; }
+__device__ __forceinline__ v4f ld4(const float* p) { return *(const gv4f*)p; }
+__device__ __forceinline__ void st4(float* p, v4f v) { *(gv4f*)p = v; }
+
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) v2u gv2u;
+__device__ __forceinline__ v2u ld2u(const uint16_t* p) { return *(const gv2u*)p; }
+
+template <int R>
+__device__ __forceinline__ float finish(float acc, float scale) {
+  // Power-of-two R: 1/R is exact, so the product is the correctly rounded
+  // quotient. Otherwise an IEEE division (hipcc keeps fp32 division correctly
+  // rounded by default).
+  if constexpr ((R & (R - 1)) == 0) return acc * scale;
+  else return acc / static_cast<float>(R);
+}
+
+__device__ __forceinline__ float finish_rt(float acc, int R, float scale, bool pow2) {
+  return pow2 ? acc * scale : acc / static_cast<float>(R);
+}
+
+template <int R>
+__device__ __forceinline__ v4f mean4(const v4f (&x)[R], float scale) {
+  v4f a = x[0];
+#pragma unroll
+  for (int r = 1; r < R; ++r) {
+    a.x = a.x + x[r].x;
+    a.y = a.y + x[r].y;
+    a.z = a.z + x[r].z;
+    a.w = a.w + x[r].w;
+  }
+  a.x = finish<R>(a.x, scale);
+  a.y = finish<R>(a.y, scale);
+  a.z = finish<R>(a.z, scale);
+  a.w = finish<R>(a.w, scale);
+  return a;
+}
+
+// Device clock stamps of one launch: [0] start (first block), [1] end (last
+// block to finish), [2] finished-block counter, reset by the last block.
+__device__ __forceinline__ void stamp_begin(int64_t* stamp) {
+  if (stamp != nullptr && blockIdx.x == 0 && threadIdx.x == 0) stamp[0] = static_cast<int64_t>(wall_clock64());
+}
+
+__device__ __forceinline__ void stamp_end(int64_t* stamp) {
+  if (stamp == nullptr) return;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    const unsigned long long prev = atomicAdd(reinterpret_cast<unsigned long long*>(stamp + 2), 1ull);
+    if (prev == gridDim.x - 1) {
+      stamp[1] = static_cast<int64_t>(wall_clock64());
+      stamp[2] = 0;
+    }
+  }
+}
+
+template <int R>
+struct Unroll {
+  static constexpr int value = R <= 2 ? 8 : (R <= 8 ? 4 : 2);
+};
+
+// ---------------------------------------------------------------------------
+// fused gather + mean + copy-back, one wavefront per segment
+
+template <int R>
+__global__ __launch_bounds__(kBlock) void fused_mean_kernel(const Segment* __restrict__ segs, int32_t nseg,
+                                                            float* const* __restrict__ grads, int32_t P,
+                                                            float scale, int32_t vec_ok,
+                                                            int64_t* __restrict__ stamp) {
+  constexpr int U = Unroll<R>::value;
+  stamp_begin(stamp);
+  const int s = blockIdx.x * kWavesPerBlock + wave_id();
+  if (s < nseg) {
+    const Segment g = segs[s];
+    const int len = static_cast<int>(g.len);
+    float* p[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) p[r] = grads[static_cast<int64_t>(r) * P + g.var] + g.start;
+    const int lane = lane_id();
+    int tail = 0;
+    if (vec_ok && (g.flags & kSegVecStart)) {
+      const int n4 = len >> 2;
+      int i = lane;
+      for (; i + 64 * (U - 1) < n4; i += 64 * U) {
+        v4f x[U][R];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int r = 0; r < R; ++r) x[u][r] = ld4(p[r] + 4 * (i + 64 * u));
+        // Keep all U*R loads in flight: the scheduler may not sink them
+        // between the adds (it would otherwise trade bandwidth for registers).
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const v4f m = mean4<R>(x[u], scale);
+#pragma unroll
+          for (int r = 0; r < R; ++r) st4(p[r] + 4 * (i + 64 * u), m);
+        }
+      }
+      for (; i < n4; i += 64) {
+        v4f x[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) x[r] = ld4(p[r] + 4 * i);
+        const v4f m = mean4<R>(x, scale);
+#pragma unroll
+        for (int r = 0; r < R; ++r) st4(p[r] + 4 * i, m);
+      }
+      tail = n4 * 4;
+    }
+    for (int j = tail + lane; j < len; j += 64) {
+      float x[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) x[r] = G(p[r])[j];
+      float a = x[0];
+#pragma unroll
+      for (int r = 1; r < R; ++r) a = a + x[r];
+      const float m = finish<R>(a, scale);
+#pragma unroll
+      for (int r = 0; r < R; ++r) G(p[r])[j] = m;
+    }
+  }
+  stamp_end(stamp);
+}
+
+// Any R (up to 64): runtime replica loop, same arithmetic order.
+__global__ __launch_bounds__(kBlock) void fused_mean_kernel_rt(const Segment* __restrict__ segs, int32_t nseg,
+                                                               float* const* __restrict__ grads, int32_t P,
+                                                               int32_t R, float scale, int32_t pow2,
+                                                               int64_t* __restrict__ stamp) {
+  stamp_begin(stamp);
+  const int s = blockIdx.x * kWavesPerBlock + wave_id();
+  if (s < nseg) {
+    const Segment g = segs[s];
+    const int len = static_cast<int>(g.len);
+    for (int j = lane_id(); j < len; j += 64) {
+      float a = G(grads[g.var])[g.start + j];
+      for (int r = 1; r < R; ++r) a = a + G(grads[static_cast<int64_t>(r) * P + g.var])[g.start + j];
+      const float m = finish_rt(a, R, scale, pow2 != 0);
+      for (int r = 0; r < R; ++r) G(grads[static_cast<int64_t>(r) * P + g.var])[g.start + j] = m;
+    }
+  }
+  stamp_end(stamp);
+}
+
+// ---------------------------------------------------------------------------
+// staged path
+
+// R gradients -> R flat buckets (the narrowed views of [Li] "Gradient
+// Bucketing": view.copy_(grad)).
+__global__ __launch_bounds__(kBlock) void pack_kernel(const Segment* __restrict__ segs, int32_t nseg,
+                                                      float* const* __restrict__ grads, int32_t P, int32_t R,
+                                                      float* __restrict__ flat, int64_t flat_stride,
+                                                      int64_t fbase, int32_t vec_ok, int64_t* __restrict__ stamp) {
+  stamp_begin(stamp);
+  const int s = blockIdx.x * kWavesPerBlock + wave_id();
+  if (s < nseg) {
+    const Segment g = segs[s];
+    const int len = static_cast<int>(g.len);
+    const int lane = lane_id();
+    const bool vec = vec_ok && (g.flags & kSegVecBoth) == kSegVecBoth;
+    for (int r = 0; r < R; ++r) {
+      const float* src = grads[static_cast<int64_t>(r) * P + g.var] + g.start;
+      float* dst = flat + r * flat_stride + fbase + g.boff;
+      int tail = 0;
+      if (vec) {
+        const int n4 = len >> 2;
+        for (int i = lane; i < n4; i += 64) st4(dst + 4 * i, ld4(src + 4 * i));
+        tail = n4 * 4;
+      }
+      for (int j = tail + lane; j < len; j += 64) G(dst)[j] = G(src)[j];
+    }
+  }
+  stamp_end(stamp);
+}
+
+// R flat buckets -> averaged bucket; grid-stride over contiguous v4fs.
+template <int R>
+__global__ __launch_bounds__(kBlock) void mean_kernel(const float* __restrict__ flat, int64_t flat_stride,
+                                                      int64_t fbase, int64_t n, float* __restrict__ avg,
+                                                      float scale, int64_t* __restrict__ stamp) {
+  stamp_begin(stamp);
+  const float* src = flat + fbase;
+  float* dst = avg + fbase;
+  const int64_t n4 = n >> 2;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < n4; i += stride) {
+    v4f x[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) x[r] = ld4(src + r * flat_stride + 4 * i);
+    st4(dst + 4 * i, mean4<R>(x, scale));
+  }
+  if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
+    const int64_t j = n4 * 4 + threadIdx.x;
+    float a = G(src)[j];
+#pragma unroll
+    for (int r = 1; r < R; ++r) a = a + G(src)[r * flat_stride + j];
+    G(dst)[j] = finish<R>(a, scale);
+  }
+  stamp_end(stamp);
+}
+
+__global__ __launch_bounds__(kBlock) void mean_kernel_rt(const float* __restrict__ flat, int64_t flat_stride,
+                                                         int64_t fbase, int64_t n, float* __restrict__ avg,
+                                                         int32_t R, float scale, int32_t pow2,
+                                                         int64_t* __restrict__ stamp) {
+  stamp_begin(stamp);
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+  for (int64_t j = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; j < n; j += stride) {
+    float a = G(flat)[fbase + j];
+    for (int r = 1; r < R; ++r) a = a + G(flat)[r * flat_stride + fbase + j];
+    G(avg)[fbase + j] = finish_rt(a, R, scale, pow2 != 0);
+  }
+  stamp_end(stamp);
+}
+
+// averaged bucket -> R gradients ([TP] "Internal Design": one batched copy per
+// bucket back into the grad fields).
+__global__ __launch_bounds__(kBlock) void copyback_kernel(const Segment* __restrict__ segs, int32_t nseg,
+                                                          float* const* __restrict__ grads, int32_t P, int32_t R,
+                                                          const float* __restrict__ avg, int64_t fbase,
+                                                          int32_t vec_ok, int64_t* __restrict__ stamp) {
+  stamp_begin(stamp);
+  const int s = blockIdx.x * kWavesPerBlock + wave_id();
+  if (s < nseg) {
+    const Segment g = segs[s];
+    const int len = static_cast<int>(g.len);
+    const int lane = lane_id();
+    const float* src = avg + fbase + g.boff;
+    const bool vec = vec_ok && (g.flags & kSegVecBoth) == kSegVecBoth;
+    int tail = 0;
+    if (vec) {
+      const int n4 = len >> 2;
+      for (int i = lane; i < n4; i += 64) {
+        const v4f m = ld4(src + 4 * i);
+        for (int r = 0; r < R; ++r) st4(grads[static_cast<int64_t>(r) * P + g.var] + g.start + 4 * i, m);
+      }
+      tail = n4 * 4;
+    }
+    for (int j = tail + lane; j < len; j += 64) {
+      const float m = G(src)[j];
+      for (int r = 0; r < R; ++r) G(grads[static_cast<int64_t>(r) * P + g.var])[g.start + j] = m;
+    }
+  }
+  stamp_end(stamp);
+}
+
+// ---------------------------------------------------------------------------
+// no_sync accumulation ([Li] "Gradient Accumulation (no_sync)": .grad adds up
+// across backward passes). One wavefront per (segment, replica).
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);   // exact widening
+}
+
+template <bool BF16, bool FIRST>
+__global__ __launch_bounds__(kBlock) void accumulate_kernel(const Segment* __restrict__ segs, int32_t nseg,
+                                                            float* const* __restrict__ grads,
+                                                            const void* const* __restrict__ steps, int32_t P,
+                                                            int32_t R, int32_t vec_ok) {
+  constexpr int U = 4;
+  const int64_t w = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave_id();
+  if (w >= static_cast<int64_t>(nseg) * R) return;
+  const int r = static_cast<int>(w / nseg);
+  const Segment g = segs[w - static_cast<int64_t>(r) * nseg];
+  const int len = static_cast<int>(g.len);
+  const int64_t k = static_cast<int64_t>(r) * P + g.var;
+  float* acc = grads[k] + g.start;
+  const int lane = lane_id();
+  int tail = 0;
+  if (BF16) {
+    const uint16_t* st = static_cast<const uint16_t*>(steps[k]) + g.start;
+    if (vec_ok && (g.flags & kSegVecStart)) {
+      const int n4 = len >> 2;
+      int i = lane;
+      for (; i + 64 * (U - 1) < n4; i += 64 * U) {
+        v2u b[U];
+        v4f a[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          b[u] = ld2u(st + 4 * (i + 64 * u));
+          if (!FIRST) a[u] = ld4(acc + 4 * (i + 64 * u));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          v4f s4;
+          s4.x = __uint_as_float(b[u].x << 16);
+          s4.y = __uint_as_float(b[u].x & 0xffff0000u);
+          s4.z = __uint_as_float(b[u].y << 16);
+          s4.w = __uint_as_float(b[u].y & 0xffff0000u);
+          if (!FIRST) {
+            s4.x = a[u].x + s4.x;
+            s4.y = a[u].y + s4.y;
+            s4.z = a[u].z + s4.z;
+            s4.w = a[u].w + s4.w;
+          }
+          st4(acc + 4 * (i + 64 * u), s4);
+        }
+      }
+      for (; i < n4; i += 64) {
+        const v2u b = ld2u(st + 4 * i);
+        v4f s4;
+        s4.x = __uint_as_float(b.x << 16);
+        s4.y = __uint_as_float(b.x & 0xffff0000u);
+        s4.z = __uint_as_float(b.y << 16);
+        s4.w = __uint_as_float(b.y & 0xffff0000u);
+        if (!FIRST) {
+          const v4f a = ld4(acc + 4 * i);
+          s4.x = a.x + s4.x;
+          s4.y = a.y + s4.y;
+          s4.z = a.z + s4.z;
+          s4.w = a.w + s4.w;
+        }
+        st4(acc + 4 * i, s4);
+      }
+      tail = n4 * 4;
+    }
+    for (int j = tail + lane; j < len; j += 64) {
+      const float s1 = bf16_to_f32(((const __attribute__((address_space(1))) uint16_t*)st)[j]);
+      G(acc)[j] = FIRST ? s1 : G(acc)[j] + s1;
+    }
+  } else {
+    const float* st = static_cast<const float*>(steps[k]) + g.start;
+    if (vec_ok && (g.flags & kSegVecStart)) {
+      const int n4 = len >> 2;
+      for (int i = lane; i < n4; i += 64) {
+        v4f s4 = ld4(st + 4 * i);
+        if (!FIRST) {
+          const v4f a = ld4(acc + 4 * i);
+          s4.x = a.x + s4.x;
+          s4.y = a.y + s4.y;
+          s4.z = a.z + s4.z;
+          s4.w = a.w + s4.w;
+        }
+        st4(acc + 4 * i, s4);
+      }
+      tail = n4 * 4;
+    }
+    for (int j = tail + lane; j < len; j += 64) G(acc)[j] = FIRST ? G(st)[j] : G(acc)[j] + G(st)[j];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launcher
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+class HipLauncher final : public Launcher {
+ public:
+  ~HipLauncher() override { release(); }
+
+  int bind(const Plan& plan, const BindArgs& a, std::string* err) override {
+    release();
+    plan_ = &plan;
+    R_ = plan.R;
+    P_ = plan.P;
+    mode_ = a.mode;
+    flags_ = a.flags;
+    compute_ = static_cast<hipStream_t>(a.compute_stream);
+    side_.clear();
+    for (void* s : a.side_streams) side_.push_back(static_cast<hipStream_t>(s));
+    side_used_.assign(side_.size(), 0);
+    pow2_ = (R_ & (R_ - 1)) == 0;
+    scale_ = 1.0f / static_cast<float>(R_);
+    vec_ok_ = 1;
+    for (void* p : a.grad_ptrs)
+      if (p != nullptr && !aligned(p, 16)) vec_ok_ = 0;
+    flat_ = nullptr;
+    avg_ = nullptr;
+    if (mode_ == 1) {
+      if (!aligned(a.workspace, 256)) {
+        *err = "bind: workspace must be 256-byte aligned";
+        return kErrArg;
+      }
+      flat_ = static_cast<float*>(a.workspace);
+      avg_ = flat_ + static_cast<int64_t>(R_) * plan.flat_elems;
+    }
+    HIP_OK(hipGetDevice(&device_), "hipGetDevice");
+
+    const size_t nptr = static_cast<size_t>(R_) * P_;
+    const size_t B = static_cast<size_t>(plan.B());
+    HIP_OK(hipMalloc(&d_grads_, std::max<size_t>(nptr, 1) * sizeof(float*)), "hipMalloc(pointer table)");
+    HIP_OK(hipMalloc(&d_segs_, std::max<size_t>(plan.segs.size(), 1) * sizeof(Segment)), "hipMalloc(segments)");
+    HIP_OK(hipMalloc(&d_stamps_, std::max<size_t>(B, 1) * 4 * sizeof(int64_t)), "hipMalloc(stamps)");
+    HIP_OK(hipMalloc(&d_steps_, std::max<size_t>(nptr, 1) * kStepSlots * sizeof(void*)), "hipMalloc(step tables)");
+    HIP_OK(hipHostMalloc(&h_steps_, std::max<size_t>(nptr, 1) * kStepSlots * sizeof(void*), hipHostMallocDefault),
+           "hipHostMalloc(step staging)");
+    if (nptr)
+      HIP_OK(hipMemcpyAsync(d_grads_, a.grad_ptrs.data(), nptr * sizeof(float*), hipMemcpyHostToDevice, compute_),
+             "upload pointer table");
+    if (!plan.segs.empty())
+      HIP_OK(hipMemcpyAsync(d_segs_, plan.segs.data(), plan.segs.size() * sizeof(Segment), hipMemcpyHostToDevice,
+                            compute_),
+             "upload segment table");
+    HIP_OK(hipMemsetAsync(d_stamps_, 0, std::max<size_t>(B, 1) * 4 * sizeof(int64_t), compute_), "clear stamps");
+    HIP_OK(hipStreamSynchronize(compute_), "bind: synchronize");
+
+    ev_ready_.assign(B, nullptr);
+    for (auto& e : ev_ready_) HIP_OK(hipEventCreateWithFlags(&e, hipEventDisableTiming), "hipEventCreate");
+    ev_done_.assign(side_.size(), nullptr);
+    for (auto& e : ev_done_) HIP_OK(hipEventCreateWithFlags(&e, hipEventDisableTiming), "hipEventCreate");
+    ev_slot_.assign(kStepSlots, nullptr);
+    for (auto& e : ev_slot_) HIP_OK(hipEventCreateWithFlags(&e, hipEventDisableTiming), "hipEventCreate");
+    slot_valid_.assign(kStepSlots, 0);
+    slot_recorded_.assign(kStepSlots, 0);
+    next_slot_ = 0;
+    if (flags_ & 2) {
+      ev_t0_.assign(B * kTimeRing, nullptr);
+      ev_t1_.assign(B * kTimeRing, nullptr);
+      for (auto& e : ev_t0_) HIP_OK(hipEventCreate(&e), "hipEventCreate");
+      for (auto& e : ev_t1_) HIP_OK(hipEventCreate(&e), "hipEventCreate");
+    }
+    return kOk;
+  }
+
+  int launch(int32_t first, int32_t last, int64_t iteration, std::string* err) override {
+    const size_t ring = static_cast<size_t>(iteration % kTimeRing) * plan_->B();
+    HIP_OK(hipEventRecord(ev_ready_[first], compute_), "hipEventRecord(ready)");
+    uint32_t waited = 0;
+    for (int32_t b = first; b <= last; ++b) {
+      const size_t si = static_cast<size_t>(b) % side_.size();
+      hipStream_t s = side_[si];
+      if (!(waited & (1u << si))) {
+        HIP_OK(hipStreamWaitEvent(s, ev_ready_[first], 0), "hipStreamWaitEvent(ready)");
+        waited |= 1u << si;
+      }
+      side_used_[si] = 1;
+      if (flags_ & 2) HIP_OK(hipEventRecord(ev_t0_[ring + b], s), "hipEventRecord(t0)");
+      const int rc = enqueue_bucket(b, s, err);
+      if (rc != kOk) return rc;
+      if (flags_ & 2) HIP_OK(hipEventRecord(ev_t1_[ring + b], s), "hipEventRecord(t1)");
+    }
+    return kOk;
+  }
+
+  int join(std::string* err) override {
+    for (size_t i = 0; i < side_.size(); ++i) {
+      if (!side_used_[i]) continue;
+      HIP_OK(hipEventRecord(ev_done_[i], side_[i]), "hipEventRecord(done)");
+      HIP_OK(hipStreamWaitEvent(compute_, ev_done_[i], 0), "hipStreamWaitEvent(done)");
+      side_used_[i] = 0;
+    }
+    return kOk;
+  }
+
+  int accumulate(void* const* step_ptrs, int32_t step_dtype, bool first, std::string* err) override {
+    const size_t nptr = static_cast<size_t>(R_) * P_;
+    if (plan_->segs.empty()) return kOk;
+    int vec = vec_ok_;
+    const uintptr_t need = step_dtype == 1 ? 8 : 16;
+    for (size_t i = 0; i < nptr; ++i) {
+      if (step_ptrs[i] == nullptr && plan_->numel[i % P_] > 0) {
+        *err = "no_sync_accumulate: NULL step pointer";
+        return kErrArg;
+      }
+      if (step_ptrs[i] != nullptr && !aligned(step_ptrs[i], need)) vec = 0;
+    }
+    // Step pointer tables go through a small ring of device slots; a table
+    // seen recently is reused without another upload.
+    int slot = -1;
+    for (int k = 0; k < kStepSlots; ++k)
+      if (slot_valid_[k] && std::memcmp(h_steps_ + k * nptr, step_ptrs, nptr * sizeof(void*)) == 0) slot = k;
+    if (slot < 0) {
+      slot = next_slot_;
+      next_slot_ = (next_slot_ + 1) % kStepSlots;
+      if (slot_recorded_[slot]) HIP_OK(hipEventSynchronize(ev_slot_[slot]), "hipEventSynchronize(slot)");
+      std::memcpy(h_steps_ + slot * nptr, step_ptrs, nptr * sizeof(void*));
+      HIP_OK(hipMemcpyAsync(d_steps_ + slot * nptr, h_steps_ + slot * nptr, nptr * sizeof(void*),
+                            hipMemcpyHostToDevice, compute_),
+             "upload step table");
+      HIP_OK(hipEventRecord(ev_slot_[slot], compute_), "hipEventRecord(slot)");
+      slot_recorded_[slot] = 1;
+      slot_valid_[slot] = 1;
+    }
+    const int32_t nseg = static_cast<int32_t>(plan_->segs.size());
+    const int64_t waves = static_cast<int64_t>(nseg) * R_;
+    const dim3 grid(static_cast<unsigned>((waves + kWavesPerBlock - 1) / kWavesPerBlock));
+    const void* const* tab = d_steps_ + slot * nptr;
+    if (step_dtype == 1) {
+      if (first)
+        hipLaunchKernelGGL((accumulate_kernel<true, true>), grid, dim3(kBlock), 0, compute_, d_segs_, nseg,
+                           d_grads_, tab, P_, R_, vec);
+      else
+        hipLaunchKernelGGL((accumulate_kernel<true, false>), grid, dim3(kBlock), 0, compute_, d_segs_, nseg,
+                           d_grads_, tab, P_, R_, vec);
+    } else {
+      if (first)
+        hipLaunchKernelGGL((accumulate_kernel<false, true>), grid, dim3(kBlock), 0, compute_, d_segs_, nseg,
+                           d_grads_, tab, P_, R_, vec);
+      else
+        hipLaunchKernelGGL((accumulate_kernel<false, false>), grid, dim3(kBlock), 0, compute_, d_segs_, nseg,
+                           d_grads_, tab, P_, R_, vec);
+    }
+    HIP_OK(hipGetLastError(), "launch accumulate_kernel");
+    return kOk;
+  }
+
+  int read_stamps(const std::vector<LaunchRecord>& log, std::vector<int64_t>* t0, std::vector<int64_t>* t1,
+                  std::string* err) override {
+    const size_t B = static_cast<size_t>(plan_->B());
+    std::vector<int64_t> h(std::max<size_t>(B, 1) * 4, 0);
+    HIP_OK(hipMemcpy(h.data(), d_stamps_, h.size() * sizeof(int64_t), hipMemcpyDeviceToHost), "read stamps");
+    t0->resize(log.size());
+    t1->resize(log.size());
+    for (size_t i = 0; i < log.size(); ++i) {
+      (*t0)[i] = h[static_cast<size_t>(log[i].bucket) * 4 + 0];
+      (*t1)[i] = h[static_cast<size_t>(log[i].bucket) * 4 + 1];
+    }
+    return kOk;
+  }
+
+  int read_times(int64_t iteration, const std::vector<LaunchRecord>& log, std::vector<float>* ms,
+                 std::string* err) override {
+    if (!(flags_ & 2)) {
+      *err = "launch timing was not enabled at bind";
+      return kErrState;
+    }
+    const size_t ring = static_cast<size_t>(iteration % kTimeRing) * plan_->B();
+    ms->resize(log.size());
+    for (size_t i = 0; i < log.size(); ++i) {
+      const size_t b = ring + static_cast<size_t>(log[i].bucket);
+      HIP_OK(hipEventSynchronize(ev_t1_[b]), "hipEventSynchronize(t1)");
+      HIP_OK(hipEventElapsedTime(&(*ms)[i], ev_t0_[b], ev_t1_[b]), "hipEventElapsedTime");
+    }
+    return kOk;
+  }
+
+  int clock_hz(int64_t* hz, std::string* err) override {
+    int dev = 0, khz = 0;
+    HIP_OK(hipGetDevice(&dev), "hipGetDevice");
+    HIP_OK(hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev), "wall clock rate");
+    *hz = static_cast<int64_t>(khz) * 1000;
+    return kOk;
+  }
+
+ private:
+  int enqueue_bucket(int32_t b, hipStream_t s, std::string* err) {
+    const int32_t s0 = plan_->seg_first[b];
+    const int32_t nseg = plan_->seg_first[b + 1] - s0;
+    if (nseg == 0) return kOk;                 // bucket of empty tensors
+    const Segment* segs = d_segs_ + s0;
+    int64_t* stamp = (flags_ & 1) ? d_stamps_ + static_cast<int64_t>(b) * 4 : nullptr;
+    const dim3 grid(static_cast<unsigned>((nseg + kWavesPerBlock - 1) / kWavesPerBlock));
+    const dim3 block(kBlock);
+    if (mode_ == 0) {
+      switch (R_) {
+#define DDPB_FUSED_CASE(RR)                                                                               \
+  case RR:                                                                                                \
+    hipLaunchKernelGGL((fused_mean_kernel<RR>), grid, block, 0, s, segs, nseg, d_grads_, P_, scale_, vec_ok_, \
+                       stamp);                                                                            \
+    break;
+        DDPB_FUSED_CASE(1) DDPB_FUSED_CASE(2) DDPB_FUSED_CASE(3) DDPB_FUSED_CASE(4)
+        DDPB_FUSED_CASE(5) DDPB_FUSED_CASE(6) DDPB_FUSED_CASE(7) DDPB_FUSED_CASE(8)
+        DDPB_FUSED_CASE(9) DDPB_FUSED_CASE(10) DDPB_FUSED_CASE(11) DDPB_FUSED_CASE(12)
+        DDPB_FUSED_CASE(13) DDPB_FUSED_CASE(14) DDPB_FUSED_CASE(15) DDPB_FUSED_CASE(16)
+#undef DDPB_FUSED_CASE
+        default:
+          hipLaunchKernelGGL(fused_mean_kernel_rt, grid, block, 0, s, segs, nseg, d_grads_, P_, R_, scale_,
+                             pow2_ ? 1 : 0, stamp);
+      }
+      HIP_OK(hipGetLastError(), "launch fused_mean_kernel");
+      return kOk;
+    }
+    // staged: pack, mean, copy-back on the same side stream
+    const int64_t fbase = plan_->flat_base[b];
+    const int64_t n = plan_->bucket_elems[b];
+    const int64_t stride = plan_->flat_elems;
+    hipLaunchKernelGGL(pack_kernel, grid, block, 0, s, segs, nseg, d_grads_, P_, R_, flat_, stride, fbase, vec_ok_,
+                       stamp);
+    HIP_OK(hipGetLastError(), "launch pack_kernel");
+    const int64_t n4 = std::max<int64_t>(n >> 2, 1);
+    const dim3 mgrid(static_cast<unsigned>(std::min<int64_t>((n4 + kBlock - 1) / kBlock, 2048)));
+    switch (R_) {
+#define DDPB_MEAN_CASE(RR)                                                                                   \
+  case RR:                                                                                                   \
+    hipLaunchKernelGGL((mean_kernel<RR>), mgrid, block, 0, s, flat_, stride, fbase, n, avg_, scale_, nullptr); \
+    break;
+      DDPB_MEAN_CASE(1) DDPB_MEAN_CASE(2) DDPB_MEAN_CASE(3) DDPB_MEAN_CASE(4)
+      DDPB_MEAN_CASE(5) DDPB_MEAN_CASE(6) DDPB_MEAN_CASE(7) DDPB_MEAN_CASE(8)
+      DDPB_MEAN_CASE(9) DDPB_MEAN_CASE(10) DDPB_MEAN_CASE(11) DDPB_MEAN_CASE(12)
+      DDPB_MEAN_CASE(13) DDPB_MEAN_CASE(14) DDPB_MEAN_CASE(15) DDPB_MEAN_CASE(16)
+#undef DDPB_MEAN_CASE
+      default:
+        hipLaunchKernelGGL(mean_kernel_rt, mgrid, block, 0, s, flat_, stride, fbase, n, avg_, R_, scale_,
+                           pow2_ ? 1 : 0, nullptr);
+    }
+    HIP_OK(hipGetLastError(), "launch mean_kernel");
+    hipLaunchKernelGGL(copyback_kernel, grid, block, 0, s, segs, nseg, d_grads_, P_, R_, avg_, fbase, vec_ok_,
+                       nullptr);
+    HIP_OK(hipGetLastError(), "launch copyback_kernel");
+    return kOk;
+  }
+
+  void release() {
+    for (auto e : ev_ready_) if (e) (void)hipEventDestroy(e);
+    for (auto e : ev_done_) if (e) (void)hipEventDestroy(e);
+    for (auto e : ev_slot_) if (e) (void)hipEventDestroy(e);
+    for (auto e : ev_t0_) if (e) (void)hipEventDestroy(e);
+    for (auto e : ev_t1_) if (e) (void)hipEventDestroy(e);
+    ev_ready_.clear();
+    ev_done_.clear();
+    ev_slot_.clear();
+    ev_t0_.clear();
+    ev_t1_.clear();
+    if (d_grads_) (void)hipFree(d_grads_);
+    if (d_segs_) (void)hipFree(d_segs_);
+    if (d_stamps_) (void)hipFree(d_stamps_);
+    if (d_steps_) (void)hipFree(d_steps_);
+    if (h_steps_) (void)hipHostFree(h_steps_);
+    d_grads_ = nullptr;
+    d_segs_ = nullptr;
+    d_stamps_ = nullptr;
+    d_steps_ = nullptr;
+    h_steps_ = nullptr;
+  }
+
+  const Plan* plan_ = nullptr;
+  int32_t R_ = 0, P_ = 0, mode_ = 0, flags_ = 0;
+  int device_ = 0;
+  bool pow2_ = true;
+  float scale_ = 1.0f;
+  int32_t vec_ok_ = 1;
+  hipStream_t compute_ = nullptr;
+  std::vector<hipStream_t> side_;
+  std::vector<uint8_t> side_used_;
+  float** d_grads_ = nullptr;
+  Segment* d_segs_ = nullptr;
+  int64_t* d_stamps_ = nullptr;
+  void** d_steps_ = nullptr;
+  void** h_steps_ = nullptr;
+  float* flat_ = nullptr;
+  float* avg_ = nullptr;
+  std::vector<hipEvent_t> ev_ready_, ev_done_, ev_slot_, ev_t0_, ev_t1_;
+  std::vector<uint8_t> slot_valid_, slot_recorded_;
+  int next_slot_ = 0;
+};
+
+}  // namespace
+
+std::unique_ptr<Launcher> make_launcher() { return std::make_unique<HipLauncher>(); }
+
+}  // namespace ddpb

@@ -1,0 +1,149 @@
+"""Python front end of the bucketed gradient reducer.
+
+PyTorch supplies device memory and streams; every step of the path runs in the
+native library (``include/ddpb.h``). The class keeps references to the tensors
+and streams it was bound to, so the caching allocator cannot hand their memory
+out while side-stream kernels still use it.
+"""
+from __future__ import annotations
+
+from typing import List, Optional, Sequence
+
+from . import _abi
+from ._abi import BF16, F32, MODE_FUSED, MODE_STAGED, BIND_DEVICE_TIMESTAMPS, BIND_TIME_LAUNCHES  # noqa: F401
+
+MiB = 1 << 20
+
+
+class Reducer:
+    def __init__(self, shapes: Sequence[Sequence[int]], R: int, bucket_cap_bytes: int = 25 * MiB,
+                 lib: Optional[_abi.Lib] = None):
+        self.lib = lib if lib is not None else _abi.lib()
+        self.shapes = [tuple(int(d) for d in s) for s in shapes]
+        self.P = len(self.shapes)
+        self.R = int(R)
+        self.cap = int(bucket_cap_bytes)
+        self.h = self.lib.reducer_create(self.shapes, F32, self.cap, self.R)
+        self._keep = []
+
+    # -- plan queries -------------------------------------------------------------
+    @property
+    def num_buckets(self) -> int:
+        return self.lib.num_buckets(self.h)
+
+    def buckets(self) -> List[List[int]]:
+        return [self.lib.get_bucket(self.h, b)[0] for b in range(self.num_buckets)]
+
+    def bucket_bytes(self) -> List[int]:
+        return [self.lib.get_bucket(self.h, b)[1] for b in range(self.num_buckets)]
+
+    def locator(self, v: int):
+        return self.lib.get_locator(self.h, v)
+
+    def workspace_bytes(self, mode: int = MODE_FUSED) -> int:
+        return self.lib.workspace_bytes(self.h, mode)
+
+    # -- binding -------------------------------------------------------------------
+    def bind(self, grads, compute_stream=None, side_streams=None, mode: int = MODE_FUSED, flags: int = 0):
+        """grads[r][v]: contiguous fp32 CUDA tensor with the v-th shape's numel."""
+        import torch
+        if len(grads) != self.R or any(len(row) != self.P for row in grads):
+            raise ValueError("grads must be R x P")
+        dev = None
+        ptrs = []
+        for r in range(self.R):
+            for v in range(self.P):
+                t = grads[r][v]
+                n = 1
+                for d in self.shapes[v]:
+                    n *= d
+                if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or t.numel() != n:
+                    raise ValueError(f"grads[{r}][{v}] must be a contiguous fp32 CUDA tensor of {n} elements")
+                dev = t.device if dev is None else dev
+                ptrs.append(t.data_ptr())
+        if dev is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        compute = compute_stream if compute_stream is not None else torch.cuda.current_stream(dev)
+        sides = list(side_streams) if side_streams else [torch.cuda.Stream(device=dev)]
+        nbytes = self.lib.workspace_bytes(self.h, mode)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
+        self._keep = [grads, ws, compute, sides]
+        self.compute_stream, self.side_streams, self.workspace = compute, sides, ws
+        self.lib.bind(self.h, ptrs, ws.data_ptr() if ws is not None else 0, nbytes, compute.cuda_stream,
+                      [s.cuda_stream for s in sides], mode, flags)
+
+    def bind_ptrs(self, ptrs: Sequence[int], workspace: int = 0, ws_bytes: int = 0, compute_stream: int = 0,
+                  side_streams: Sequence[int] = (0,), mode: int = MODE_FUSED, flags: int = 0):
+        """Raw-pointer bind (used by the host-only tests)."""
+        self.lib.bind(self.h, ptrs, workspace, ws_bytes, compute_stream, side_streams, mode, flags)
+
+    # -- iteration -------------------------------------------------------------------
+    def ensure_prior_reduction_finished(self):
+        self.lib.ensure_prior_reduction_finished(self.h)
+
+    def mark_ready(self, v: int):
+        self.lib.mark_ready(self.h, v)
+
+    def mark_ready_many(self, vs: Sequence[int]):
+        self.lib.mark_ready_many(self.h, vs)
+
+    def finalize(self):
+        self.lib.finalize(self.h)
+
+    def set_sync(self, enabled: bool):
+        self.lib.set_sync(self.h, enabled)
+
+    def reset(self):
+        self.lib.reset(self.h)
+
+    def sync(self, order: Optional[Sequence[int]] = None):
+        """One synchronisation: every hook in ``order`` (default: last-defined
+        parameter first), then finalize."""
+        if order is None:
+            order = range(self.P - 1, -1, -1)
+        mr = self.lib.mark_ready
+        h = self.h
+        for v in order:
+            mr(h, v)
+        self.lib.finalize(h)
+
+    def no_sync_accumulate(self, steps, first_step: bool):
+        """steps[r][v]: contiguous fp32 or bf16 CUDA tensor per replica/variable."""
+        import torch
+        dt = steps[0][0].dtype
+        code = {torch.float32: F32, torch.bfloat16: BF16}.get(dt)
+        if code is None:
+            raise ValueError("step gradients must be fp32 or bf16")
+        ptrs = []
+        for r in range(self.R):
+            for v in range(self.P):
+                t = steps[r][v]
+                if t.dtype != dt or not t.is_contiguous():
+                    raise ValueError("step gradients must be contiguous and of one dtype")
+                ptrs.append(t.data_ptr())
+        self.lib.no_sync_accumulate(self.h, ptrs, code, first_step)
+
+    # -- diagnostics -------------------------------------------------------------------
+    def launch_log(self, with_stamps: bool = False):
+        return self.lib.get_launch_log(self.h, with_stamps)
+
+    def launch_times_ms(self, iterations_ago: int = 0) -> List[float]:
+        return self.lib.get_launch_times(self.h, iterations_ago)
+
+    def device_clock_hz(self) -> int:
+        return self.lib.device_clock_hz(self.h)
+
+    def close(self):
+        if self.h:
+            self.lib.destroy(self.h)
+            self.h = None
+            self._keep = []
+
+    def __del__(self):
+        import sys
+        if sys.is_finalizing():      # the HIP runtime may already be gone
+            return
+        try:
+            self.close()
+        except Exception:
+            pass

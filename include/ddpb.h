@@ -1,0 +1,223 @@
+/*
+ * ddpb.h -- C ABI of the bucketed gradient reducer for MI355X (gfx950).
+ *
+ * The library implements the gradient-reduction hot path of a data-parallel
+ * wrapper as these pages describe it:
+ *   [Li]   "PyTorch Distributed: Experiences on Accelerating Data Parallel
+ *          Training" (paper-graph-ui summary of arXiv 2006.15704), §3.4,
+ *          subsections "Gradient Bucketing", "Overlapping Computation with
+ *          Communication", "Gradient Accumulation (no_sync)";
+ *   [TP]   "Distributed Data Parallel" (tensorplay.cn notes), "Internal Design",
+ *          "When a parameter never receives a gradient", "Gradient sync you can
+ *          turn off";
+ *   [C30]  "NCCL 专家课程 30：DDP Reducer、Bucket 与计算通信重叠" (blog.cptz.space),
+ *          sections "Variable 到 Bucket", "Bucket 必须按序发起",
+ *          "bucket_cap_mb 不是张量切分器", "Finalize Backward 与梯度可见性";
+ *   [PDTI] "PyTorch Distributed Training Internals", §2 and §3.
+ *
+ * R data-parallel replicas live in one GPU's HBM. The all-reduce of a bucket
+ * is emulated by an in-HBM elementwise mean over the R replicas' gradients,
+ * summed in replica order 0..R-1 in fp32 and divided once by R (IEEE,
+ * round to nearest even), after which the mean is written back into every
+ * replica's gradient. There is no communication between GPUs.
+ *
+ * Conventions
+ *  - Every call returns a status code (DDPB_OK or a negative DDPB_E_*); no
+ *    C++ exception crosses the ABI. ddpb_last_error() describes the last
+ *    failure on the calling thread.
+ *  - Device pointers are HIP device addresses of memory the caller owns
+ *    (allocated by PyTorch); they must stay valid until ddpb_destroy or the
+ *    next ddpb_bind. Host pointers are read during the call only.
+ *  - Streams are hipStream_t values passed as void*. The library owns its
+ *    hipEvents and a small device copy of its pointer and segment tables.
+ *  - A handle is driven by one host thread; the API is not thread-safe.
+ *  - "Replica-major" arrays of R*P pointers hold replica r's variable v at
+ *    index r*P + v.
+ */
+#ifndef DDPB_H
+#define DDPB_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ddpb_reducer* ddpb_t;
+
+/* element types */
+enum { DDPB_F32 = 0, DDPB_BF16 = 1 };
+
+/* kernel modes for ddpb_bind */
+enum {
+  DDPB_MODE_FUSED = 0,  /* one kernel per bucket: gather, mean, write back; no flat copy */
+  DDPB_MODE_STAGED = 1  /* three kernels per bucket: pack into flat buckets, mean, copy back */
+};
+
+/* flags for ddpb_bind */
+enum {
+  DDPB_BIND_DEVICE_TIMESTAMPS = 1, /* kernels stamp start/end device clock into the launch log */
+  DDPB_BIND_TIME_LAUNCHES = 2      /* hipEvents around each bucket's kernels (ddpb_get_launch_times) */
+};
+
+/* status codes */
+enum {
+  DDPB_OK = 0,
+  DDPB_E_ARG = -1,          /* bad argument (null pointer, size, dtype, misaligned buffer) */
+  DDPB_E_INDEX = -2,        /* variable or bucket index out of range */
+  DDPB_E_DOUBLE_READY = -3, /* a variable was marked ready twice in one iteration */
+  DDPB_E_INCOMPLETE = -4,   /* the iteration did not reduce every bucket */
+  DDPB_E_STATE = -5,        /* call not valid in the current state (e.g. not bound) */
+  DDPB_E_HIP = -6,          /* a HIP runtime call failed */
+  DDPB_E_NOMEM = -7         /* host or device allocation failed */
+};
+
+/* ---------------------------------------------------------------------------
+ * Construction and plan ([Li] "Gradient Bucketing"; [C30] "Variable 到 Bucket",
+ * "bucket_cap_mb 不是张量切分器").
+ */
+
+/* Plan the buckets for P parameters given in Model.parameters() order.
+ *   shapes     concatenated dims of all parameters (sum(ndims) entries, >= 0)
+ *   ndims      ndims[v] = number of dims of parameter v (0 = scalar, numel 1)
+ *   dtype      gradient/bucket element type; DDPB_F32 only
+ *   bucket_cap_bytes  the cap (>= 0). Parameters are visited in reverse
+ *              order; each whole tensor joins the open bucket and the bucket
+ *              closes once its byte size is >= the cap (so 0 = one bucket per
+ *              tensor, and a tensor larger than the cap forms one larger
+ *              bucket). Bucket 0 holds the last-defined parameters.
+ *   R          number of emulated replicas, 1..64
+ * Host-only: no device is touched. *out receives the handle. */
+int ddpb_reducer_create(const int64_t* shapes, const int32_t* ndims, int32_t P,
+                        int32_t dtype, int64_t bucket_cap_bytes, int32_t R, ddpb_t* out);
+
+void ddpb_destroy(ddpb_t h);
+
+int ddpb_num_buckets(ddpb_t h, int32_t* B);
+
+/* The locator of variable v: bucket index, position inside the bucket, and
+ * element offset/length of its narrowed view of the flat bucket. */
+int ddpb_get_locator(ddpb_t h, int32_t v, int32_t* bucket, int32_t* intra,
+                     int64_t* offset, int64_t* length);
+
+/* Bucket b: number of member variables, byte size, and (if vars != NULL) its
+ * member variable indices in bucket order (vars must hold nvars entries). */
+int ddpb_get_bucket(ddpb_t h, int32_t b, int32_t* nvars, int64_t* bytes, int32_t* vars);
+
+/* The device work table. Each bucket's members are cut into segments of at
+ * most seg_elems elements; one wavefront processes one segment. Segments are
+ * stored bucket by bucket; bucket b owns [first, first + count). */
+int ddpb_num_segments(ddpb_t h, int32_t* n, int64_t* seg_elems);
+int ddpb_get_bucket_segments(ddpb_t h, int32_t b, int32_t* first, int32_t* count);
+int ddpb_get_segment(ddpb_t h, int32_t s, int32_t* var, int32_t* bucket,
+                     int64_t* start, int64_t* length, int64_t* bucket_offset);
+
+/* ---------------------------------------------------------------------------
+ * Binding memory and streams.
+ */
+
+/* Device bytes of caller-provided workspace needed by a mode: 0 for FUSED;
+ * for STAGED, R per-replica flat copies of every bucket plus one averaged
+ * copy (each bucket starts on a 256-byte boundary). */
+int ddpb_workspace_bytes(ddpb_t h, int32_t mode, int64_t* bytes);
+
+/* Attach device memory and streams.
+ *   grad_ptrs      R*P device pointers (replica-major) to each replica's fp32
+ *                  gradient of each variable, numel[v] contiguous elements.
+ *                  The reducer reads them and writes the averaged values back
+ *                  in place.
+ *   workspace      device buffer of >= ddpb_workspace_bytes(mode) bytes (may
+ *                  be NULL when that is 0), 256-byte aligned.
+ *   compute_stream stream on which gradients are produced (hipStream_t).
+ *   side_streams   n_side >= 1 streams for the reduction kernels; bucket b
+ *                  runs on side_streams[b % n_side].
+ *   mode, flags    DDPB_MODE_*, DDPB_BIND_*.
+ * Synchronizes the compute stream once to upload the tables. Not allowed
+ * while an iteration is in progress. */
+int ddpb_bind(ddpb_t h, void* const* grad_ptrs, void* workspace, int64_t ws_bytes,
+              void* compute_stream, void* const* side_streams, int32_t n_side,
+              int32_t mode, int32_t flags);
+
+/* ---------------------------------------------------------------------------
+ * One iteration ([Li] "Overlapping Computation with Communication";
+ * [C30] "Bucket 必须按序发起", "Finalize Backward 与梯度可见性").
+ */
+
+/* The check a wrapper's forward makes before a new iteration: returns
+ * DDPB_E_INCOMPLETE (and latches that state until ddpb_reset) when the
+ * previous iteration marked variables ready but did not finish reducing
+ * every bucket ([TP] "When a parameter never receives a gradient"). */
+int ddpb_ensure_prior_reduction_finished(ddpb_t h);
+
+/* Hook for variable v: its gradient is final on every replica, ordered on the
+ * compute stream. Decrements the pending count of v's bucket. When the count
+ * reaches zero and every earlier bucket has been launched, launches that
+ * bucket and then every following bucket that is already complete, in index
+ * order: it records an event on the compute stream, makes the side stream
+ * wait for it and enqueues the bucket's kernels. A bucket that completes
+ * before an earlier one waits (parked) until the earlier one is launched.
+ * With sync disabled it returns DDPB_OK and does nothing.
+ * Errors: DDPB_E_INDEX, DDPB_E_DOUBLE_READY, DDPB_E_STATE (not bound),
+ * DDPB_E_INCOMPLETE (latched failure), DDPB_E_HIP. */
+int ddpb_mark_ready(ddpb_t h, int32_t v);
+
+/* Same as calling ddpb_mark_ready for vs[0..n-1] in order; stops at the first
+ * error and returns it. */
+int ddpb_mark_ready_many(ddpb_t h, const int32_t* vs, int32_t n);
+
+/* End of backward: every bucket must have been launched (else
+ * DDPB_E_INCOMPLETE, latched). Records a completion event on every side
+ * stream and makes the compute stream wait for them, so later work on the
+ * compute stream sees the averaged gradients without a host synchronization;
+ * then resets the per-iteration state. A no-op while sync is disabled and no
+ * variable was marked. */
+int ddpb_finalize(ddpb_t h);
+
+/* The no_sync() switch ([Li] "Gradient Accumulation (no_sync)"; [TP] "Gradient
+ * sync you can turn off"): enabled = 0 makes ddpb_mark_ready a no-op.
+ * DDPB_E_STATE if an iteration is in progress. */
+int ddpb_set_sync(ddpb_t h, int32_t enabled);
+
+/* Local gradient accumulation of one backward pass into the bound fp32
+ * gradients, on the compute stream: grad = float(step) when first_step != 0,
+ * grad += float(step) otherwise, elementwise for every replica and variable.
+ *   step_ptrs   R*P device pointers (replica-major), numel[v] elements each
+ *   step_dtype  DDPB_F32 or DDPB_BF16 (widened exactly to fp32) */
+int ddpb_no_sync_accumulate(ddpb_t h, void* const* step_ptrs, int32_t step_dtype,
+                            int32_t first_step);
+
+/* Clears a latched DDPB_E_INCOMPLETE and the per-iteration state. Buckets
+ * already enqueued keep running. */
+int ddpb_reset(ddpb_t h);
+
+/* ---------------------------------------------------------------------------
+ * Diagnostics.
+ */
+
+/* Launches of the current or last finished iteration, in launch order:
+ * bucket index, index (0-based, within the iteration) of the ddpb_mark_ready
+ * call that launched it, and, with DDPB_BIND_DEVICE_TIMESTAMPS, the device
+ * clock (wall_clock64 ticks) at kernel start and end (else 0). Device values
+ * are read with a blocking copy; synchronize the side streams first.
+ * Writes min(cap, count) entries and sets *n = count. */
+int ddpb_get_launch_log(ddpb_t h, int32_t* buckets, int32_t* trigger_call,
+                        int64_t* dev_t0, int64_t* dev_t1, int32_t cap, int32_t* n);
+
+/* With DDPB_BIND_TIME_LAUNCHES: milliseconds between the events recorded
+ * before and after each launched bucket's kernels on its side stream, in
+ * launch order, for the finalized iteration `iterations_ago` back (0 = the
+ * last one; events of the last 4 iterations are kept, else DDPB_E_INDEX).
+ * Blocks the host until those events have completed; later iterations may
+ * keep running on the device meanwhile. */
+int ddpb_get_launch_times(ddpb_t h, int32_t iterations_ago, float* ms, int32_t cap, int32_t* n);
+
+/* Device clock rate of wall_clock64 in Hz (for converting launch-log ticks). */
+int ddpb_device_clock_hz(ddpb_t h, int64_t* hz);
+
+const char* ddpb_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DDPB_H */

@@ -124,12 +124,12 @@ class Reducer:
 
     # -- hooks ---------------------------------------------------------------
     def mark_ready(self, v: int):
+        if not (0 <= v < self.P):
+            raise IndexError(v)
         if not self.sync_enabled:
             return
         if self.failed:
             raise ReductionIncomplete("prior iteration did not finish reducing every bucket")
-        if not (0 <= v < self.P):
-            raise IndexError(v)
         if self.ready[v]:
             raise DoubleReady(v)
         self.ready[v] = True

@@ -1,0 +1,401 @@
+"""GPU parity: the HIP path, called through the C ABI, against the oracle,
+bit for bit (0 ULP) on the same seeded inputs.
+
+Small cases span several segments and ragged tails and run the whole oracle;
+the full-size workloads compare every element where the oracle can afford it
+(ResNet-50 shapes) or sampled tensors plus replica-equality over everything
+(BERT-large, BERT-base no_sync) in the launch configuration the bench times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import ddp_bucketed_gradient_amd as D
+from gpu_util import require_gpu, say, alloc_grads, fill_from_host, snapshot, assert_bits_equal
+from oracle import reducer as OR
+from oracle import linear10 as OL
+from workloads import shapes as WS, gen as WG, configs as WC
+
+pytestmark = pytest.mark.gpu
+MiB = 1 << 20
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+    yield
+    torch.cuda.synchronize()
+
+
+def _oracle_sync(numels, R, cap, host, order):
+    red = OR.Reducer(numels, R, cap)
+    g = [[np.array(host[r][v], np.float32, copy=True) for v in range(len(numels))] for r in range(R)]
+    red.bind(g)
+    red.sync(order)
+    return g, red.launch_log
+
+
+def _host_inputs(seed, numels, R, kind="normal"):
+    if kind == "dyadic":
+        return [[WG.dyadic(seed * 7919 + r * 131 + v, n) for v, n in enumerate(numels)] for r in range(R)]
+    return [[WG.normal(WG.seed_of(9, r, v, seed % 100), n).numpy() for v, n in enumerate(numels)]
+            for r in range(R)]
+
+
+RAGGED = [1, 3, 4, 5, 63, 64, 65, 255, 1000, 4095, 4096, 4097, 8191, 8193, 12345, 20000, 2, 777]
+
+
+@pytest.mark.parametrize("R", [1, 2, 3, 5, 8, 16])
+@pytest.mark.parametrize("mode", [D.MODE_FUSED, D.MODE_STAGED])
+def test_ragged_parity(R, mode):
+    numels = RAGGED
+    cap = 4 * 9000
+    order = WG.permutation(R * 10 + mode, len(numels))
+    say(f"ragged R={R} mode={mode} P={len(numels)} cap={cap}")
+    red = D.Reducer([(n,) for n in numels], R, cap)
+    grads = alloc_grads(numels, R)
+    red.bind(grads, mode=mode)
+    for it in range(2):
+        host = _host_inputs(it + R, numels, R, "dyadic" if (it == 1 and R == 3) else "normal")
+        fill_from_host(grads, host)
+        red.sync(order)
+        got = snapshot(grads)
+        want, log = _oracle_sync(numels, R, cap, host, order)
+        assert red.launch_log() == log
+        for v in range(len(numels)):
+            for r in range(R):
+                assert_bits_equal(got[v][r], want[r][v], f"it={it} v={v} r={r}")
+    red.close()
+
+
+@pytest.mark.parametrize("n_side", [2, 3])
+def test_multiple_side_streams(n_side):
+    numels = RAGGED * 2
+    R = 4
+    red = D.Reducer([(n,) for n in numels], R, 0)            # one bucket per tensor
+    grads = alloc_grads(numels, R)
+    sides = [torch.cuda.Stream() for _ in range(n_side)]
+    red.bind(grads, side_streams=sides)
+    host = _host_inputs(3, numels, R)
+    fill_from_host(grads, host)
+    order = list(range(len(numels) - 1, -1, -1))
+    red.sync(order)
+    got = snapshot(grads)
+    want, _ = _oracle_sync(numels, R, 0, host, order)
+    for v in range(len(numels)):
+        for r in range(R):
+            assert_bits_equal(got[v][r], want[r][v], f"v={v} r={r}")
+
+
+def test_special_values():
+    R = 3
+    vals = np.array([0.0, -0.0, 1e-45, -1e-45, 2e-45, 1.1754942e-38, 3.4e38, 3.4e38, -3.4e38,
+                     np.inf, -np.inf, np.nan, 1.0, 2.0 ** 24, 1.0, -(2.0 ** 24)], dtype=np.float32)
+    host = [[np.roll(vals, r)] for r in range(R)]
+    for RR in (2, 3, 8):
+        host = [[np.roll(vals, r * 3 + 1).copy()] for r in range(RR)]
+        for mode in (D.MODE_FUSED, D.MODE_STAGED):
+            red = D.Reducer([(vals.size,)], RR, 0)
+            grads = alloc_grads([vals.size], RR)
+            red.bind(grads, mode=mode)
+            fill_from_host(grads, host)
+            red.sync()
+            got = snapshot(grads)
+            want, _ = _oracle_sync([vals.size], RR, 0, host, [0])
+            for r in range(RR):
+                assert_bits_equal(got[0][r], want[r][0], f"R={RR} mode={mode}")
+    # subnormal results must not be flushed: (2^-149 + 2^-149) / 2
+    red = D.Reducer([(8,)], 2, 0)
+    grads = alloc_grads([8], 2)
+    red.bind(grads)
+    tiny = np.full(8, np.float32(2.0 ** -149), np.float32)
+    fill_from_host(grads, [[tiny], [tiny]])
+    red.sync()
+    assert np.array_equal(snapshot(grads)[0][0].view(np.uint32), np.ones(8, np.uint32))
+
+
+def test_unaligned_views_take_the_scalar_path():
+    numels = [5, 4096, 37, 1000]
+    R = 4
+    base = [torch.zeros(sum(numels) + 16, device="cuda") for _ in range(R)]
+    grads = []
+    for r in range(R):
+        off, row = 1, []                     # 4-byte offset: not 16-byte aligned
+        for n in numels:
+            row.append(base[r][off:off + n])
+            off += n
+        grads.append(row)
+    host = _host_inputs(11, numels, R)
+    fill_from_host(grads, host)
+    for mode in (D.MODE_FUSED, D.MODE_STAGED):
+        fill_from_host(grads, host)
+        red = D.Reducer([(n,) for n in numels], R, 4 * 2000)
+        red.bind(grads, mode=mode)
+        red.sync()
+        got = snapshot(grads)
+        want, _ = _oracle_sync(numels, R, 4 * 2000, host, list(range(len(numels) - 1, -1, -1)))
+        for v in range(len(numels)):
+            for r in range(R):
+                assert_bits_equal(got[v][r], want[r][v], f"mode={mode} v={v} r={r}")
+        red.close()
+
+
+def test_empty_tensors_and_empty_model():
+    numels = [0, 7, 0, 4100, 0]
+    R = 2
+    red = D.Reducer([(n,) for n in numels], R, 0)
+    grads = alloc_grads(numels, R)
+    red.bind(grads)
+    host = _host_inputs(2, numels, R)
+    fill_from_host(grads, host)
+    red.sync()
+    got = snapshot(grads)
+    want, _ = _oracle_sync(numels, R, 0, host, list(range(4, -1, -1)))
+    for v in (1, 3):
+        for r in range(R):
+            assert_bits_equal(got[v][r], want[r][v])
+    empty = D.Reducer([], 4)
+    empty.bind([[] for _ in range(4)])
+    empty.sync()
+
+
+def test_linear10_example():
+    """nn.Linear(10, 10), two ranks, loss mean(out^2), lr 0.001: after the
+    step every replica holds the same parameters."""
+    R = 2
+    W0, b0 = WG.linear10_init(0)                          # broadcast: every rank takes rank 0's
+    params = [[W0.clone().cuda().requires_grad_(), b0.clone().cuda().requires_grad_()] for _ in range(R)]
+    for r in range(R):
+        x = WG.linear10_batch(r).cuda()
+        out = x @ params[r][0].T + params[r][1]
+        out.square().mean().backward()
+    grads = [[p[0].grad, p[1].grad] for p in params]
+    red = D.Reducer([(10, 10), (10,)], R)
+    assert red.buckets() == [[1, 0]]
+    red.bind(grads)
+    local = snapshot(grads)
+    red.sync()
+    got = snapshot(grads)
+    host = [[local[v][r].reshape(-1) for v in range(2)] for r in range(R)]
+    want, _ = _oracle_sync([100, 10], R, 25 * MiB, host, [1, 0])
+    for v in range(2):
+        for r in range(R):
+            assert_bits_equal(got[v][r].reshape(-1), want[r][v], f"v={v} r={r}")
+    # the averaged gradient agrees with the float64 closed form to fp32 accuracy
+    cf = [OL.grads(WG.linear10_batch(r).numpy(), W0.numpy(), b0.numpy()) for r in range(R)]
+    mean_dW = (cf[0][0].astype(np.float64) + cf[1][0]) / 2
+    assert np.allclose(got[0][0], mean_dW, rtol=1e-5, atol=1e-7)
+    with torch.no_grad():
+        for r in range(R):
+            for p in params[r]:
+                p.add_(p.grad, alpha=-0.001)
+    for r in range(1, R):
+        for p, q in zip(params[r], params[0]):
+            assert torch.equal(p, q)
+
+
+def test_stream_ordering_with_delayed_producer():
+    """The last gradient is written on the compute stream behind a long chain
+    of GEMMs; the reduction on the side stream must wait for it."""
+    numels = [4096 * 3 + 5, 999, 50000]
+    R = 4
+    red = D.Reducer([(n,) for n in numels], R, 0)
+    grads = alloc_grads(numels, R)
+    for row in grads:
+        for g in row:
+            g.zero_()
+    red.bind(grads)
+    host = _host_inputs(21, numels, R)
+    staged = [[torch.from_numpy(h).cuda() for h in row] for row in host]
+    torch.cuda.synchronize()
+    a = torch.randn(2048, 2048, device="cuda")
+    for v in (2, 1, 0):                       # reverse index = bucket order
+        for _ in range(40):
+            a = torch.tanh(a @ a * 1e-3)       # delay on the compute stream
+        for r in range(R):
+            grads[r][v].copy_(staged[r][v])
+        red.mark_ready(v)                     # host does not wait
+    red.finalize()
+    got = snapshot(grads)
+    want, _ = _oracle_sync(numels, R, 0, host, [2, 1, 0])
+    for v in range(3):
+        for r in range(R):
+            assert_bits_equal(got[v][r], want[r][v], f"v={v} r={r}")
+
+
+def test_parked_buckets_and_device_stamps():
+    numels = [3000] * 12
+    R = 2
+    red = D.Reducer([(n,) for n in numels], R, 0)
+    grads = alloc_grads(numels, R)
+    red.bind(grads, flags=D.BIND_DEVICE_TIMESTAMPS | D.BIND_TIME_LAUNCHES)
+    host = _host_inputs(4, numels, R)
+    fill_from_host(grads, host)
+    order = [11, 9, 8, 10, 7, 3, 4, 5, 6, 2, 0, 1]     # buckets 0, park, ..., so launches batch up
+    red.sync(order)
+    torch.cuda.synchronize()
+    got = snapshot(grads)
+    want, log = _oracle_sync(numels, R, 0, host, order)
+    rows, t0, t1 = red.launch_log(with_stamps=True)
+    assert rows == log
+    assert [b for b, _ in rows] == list(range(12))
+    assert all(b > a for a, b in zip(t0, t0[1:]))           # one side stream: in order on the device
+    assert all(e >= s for s, e in zip(t0, t1))
+    assert all(s >= e for s, e in zip(t0[1:], t1))           # and never overlapping
+    ms = red.launch_times_ms()
+    assert len(ms) == 12 and all(m > 0 for m in ms)
+    assert red.device_clock_hz() > 0
+    for v in range(12):
+        for r in range(R):
+            assert_bits_equal(got[v][r], want[r][v])
+
+
+def test_incomplete_iteration_then_recovery():
+    numels = [100, 200, 300]
+    R = 2
+    red = D.Reducer([(n,) for n in numels], R, 0)
+    grads = alloc_grads(numels, R)
+    red.bind(grads)
+    host = _host_inputs(8, numels, R)
+    fill_from_host(grads, host)
+    red.mark_ready(2)
+    red.mark_ready(1)                 # variable 0 never gets its hook
+    with pytest.raises(D.DdpbError) as e:
+        red.finalize()
+    assert e.value.code == -4
+    with pytest.raises(D.DdpbError):
+        red.ensure_prior_reduction_finished()
+    torch.cuda.synchronize()
+    red.reset()
+    fill_from_host(grads, host)
+    red.sync()
+    got = snapshot(grads)
+    want, _ = _oracle_sync(numels, R, 0, host, [2, 1, 0])
+    for v in range(3):
+        for r in range(R):
+            assert_bits_equal(got[v][r], want[r][v])
+
+
+# --- no_sync -------------------------------------------------------------------
+
+def _oracle_nosync_one(host_steps_v, R, k):
+    """Oracle on a one-variable model: accumulate k micro-steps, then sync."""
+    n = host_steps_v[0][0].size
+    red = OR.Reducer([n], R, 0)
+    g = [[np.zeros(n, np.float32)] for _ in range(R)]
+    red.bind(g)
+    for t in range(k):
+        red.no_sync_accumulate([[host_steps_v[t][r]] for r in range(R)], first=(t == 0))
+    red.sync()
+    return [g[r][0] for r in range(R)]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_no_sync_small(dtype):
+    numels = RAGGED
+    R, k = 4, 3
+    red = D.Reducer([(n,) for n in numels], R, 4 * 10000)
+    grads = alloc_grads(numels, R)
+    red.bind(grads)
+    steps = [[[WG.normal(WG.seed_of(4, r, v, t), n, "cuda").to(dtype) for v, n in enumerate(numels)]
+              for r in range(R)] for t in range(k)]
+    red.set_sync(False)
+    for t in range(k - 1):
+        red.no_sync_accumulate(steps[t], first_step=(t == 0))
+        red.sync()                                         # hooks are no-ops
+        assert red.launch_log() == [] or t > 0
+    red.set_sync(True)
+    red.no_sync_accumulate(steps[k - 1], first_step=(k == 1))
+    red.sync()
+    torch.cuda.synchronize()
+    for v, n in enumerate(numels):
+        if dtype == torch.bfloat16:
+            hs = [[steps[t][r][v].view(torch.int16).cpu().numpy().view(np.uint16) for r in range(R)] for t in range(k)]
+        else:
+            hs = [[steps[t][r][v].cpu().numpy() for r in range(R)] for t in range(k)]
+        want = _oracle_nosync_one(hs, R, k)
+        for r in range(R):
+            assert_bits_equal(grads[r][v].cpu().numpy(), want[r], f"v={v} r={r}")
+
+
+# --- full-size workloads -----------------------------------------------------------
+
+def _device_inputs(cfg, grads, t=0):
+    for r, row in enumerate(grads):
+        for v, g in enumerate(row):
+            WG.normal(WG.seed_of(cfg, r, v, t), g.numel(), "cuda", out=g)
+
+
+def test_config2_resnet50_full():
+    w = WC.RESNET50
+    numels = w.numels()
+    say(f"{w.name}: P={len(numels)} R={w.R}")
+    red = D.Reducer([p.shape for p in w.params()], w.R, w.cap_bytes)
+    assert red.num_buckets == 4
+    grads = alloc_grads(numels, w.R)
+    red.bind(grads)
+    _device_inputs(w.cfg, grads)
+    host_in = snapshot(grads)
+    red.sync(w.ready_order())
+    got = snapshot(grads)
+    host = [[host_in[v][r] for v in range(len(numels))] for r in range(w.R)]
+    want, log = _oracle_sync(numels, w.R, w.cap_bytes, host, w.ready_order())
+    assert red.launch_log() == log
+    for v in range(len(numels)):
+        for r in range(w.R):
+            assert_bits_equal(got[v][r], want[r][v], f"v={v} r={r}")
+
+
+BERT_SAMPLE = [0, 1, 2, 3, 4, 5, 12, 13, 16, 17, 100, 200, 385, 386, 388, 389, 390]
+
+
+@pytest.mark.parametrize("cap_mib", [25, 0, 1, 5, 10, 50, 100, 200])
+def test_config3_bert_large_sampled(cap_mib):
+    w = WC.bert_large_cap(cap_mib)
+    numels = w.numels()
+    say(f"{w.name}: P={len(numels)} R={w.R}")
+    red = D.Reducer([p.shape for p in w.params()], w.R, w.cap_bytes)
+    grads = alloc_grads(numels, w.R)
+    red.bind(grads)
+    _device_inputs(w.cfg, grads)
+    before = snapshot(grads, BERT_SAMPLE)
+    red.sync(w.ready_order())
+    torch.cuda.synchronize()
+    for v in range(len(numels)):            # every replica identical everywhere
+        for r in range(1, w.R):
+            assert torch.equal(grads[r][v], grads[0][v]), (v, r)
+    for v in BERT_SAMPLE:
+        want = OR.fixed_order_mean(before[v])
+        assert_bits_equal(grads[3][v].cpu().numpy(), want, f"v={v}")
+    assert [b for b, _ in red.launch_log()] == list(range(red.num_buckets))
+
+
+def test_config4_bert_base_nosync_sampled():
+    w = WC.BERT_BASE_NOSYNC
+    numels = w.numels()
+    R, k = w.R, w.micro_steps
+    say(f"{w.name}: P={len(numels)} R={R} k={k}")
+    red = D.Reducer([p.shape for p in w.params()], R, w.cap_bytes)
+    assert red.num_buckets == 13
+    grads = alloc_grads(numels, R)
+    red.bind(grads)
+    sample = [0, 1, 5, 6, 100, 197, 198]
+    hs = {v: [] for v in sample}
+    red.set_sync(False)
+    for t in range(k):
+        steps = [[WG.normal(WG.seed_of(4, r, v, t), n, "cuda").to(torch.bfloat16) for v, n in enumerate(numels)]
+                 for r in range(R)]
+        for v in sample:
+            hs[v].append([steps[r][v].view(torch.int16).cpu().numpy().view(np.uint16) for r in range(R)])
+        if t == k - 1:
+            red.set_sync(True)
+        red.no_sync_accumulate(steps, first_step=(t == 0))
+        red.sync(w.ready_order())
+        del steps
+    torch.cuda.synchronize()
+    for v in range(len(numels)):
+        for r in range(1, R):
+            assert torch.equal(grads[r][v], grads[0][v]), (v, r)
+    for v in sample:
+        want = _oracle_nosync_one(hs[v], R, k)
+        assert_bits_equal(grads[R - 1][v].cpu().numpy(), want[0], f"v={v}")

@@ -1,0 +1,256 @@
+"""CPU tests of the native host core through the C ABI: the library loads and
+exports every declared symbol; the plan, locators and segment table agree with
+the oracle; the readiness state machine launches exactly as the oracle does;
+error codes behave as documented.
+
+The state machine runs in the host-only test build (same core.cpp/abi.cpp,
+launcher that enqueues nothing), so no GPU is needed.
+"""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import ddp_bucketed_gradient_amd as D
+from ddp_bucketed_gradient_amd import _abi
+from oracle import plan as OP
+from oracle import reducer as OR
+from workloads import shapes as WS, gen as WG
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ddpb.h")
+MiB = 1 << 20
+
+
+@pytest.fixture(scope="module")
+def host():
+    if not os.path.exists(D.HOSTONLY_LIB):
+        from ddp_bucketed_gradient_amd import build
+        build.build_hostonly()
+    return D.Lib(D.HOSTONLY_LIB)
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ddpb_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(_abi.SYMBOLS)
+
+
+@pytest.mark.parametrize("path", [D.HIP_LIB, D.HOSTONLY_LIB])
+def test_library_loads_and_exports_every_symbol(path, host):
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not built")
+    lib = D.Lib(path)
+    for name in _declared():
+        assert hasattr(lib.dll, name), name
+
+
+def _reducer(host, numels, R, cap):
+    return D.Reducer([(n,) for n in numels], R, cap, lib=host)
+
+
+def _bind_fake(red):
+    # the host-only launcher never dereferences pointers; any non-null value
+    red.bind_ptrs([0x1000 + 16 * i for i in range(red.R * red.P)], side_streams=[0])
+
+
+# --- plan -----------------------------------------------------------------------
+
+PLAN_CASES = [
+    (WS.numels(WS.linear10()), 25 * MiB),
+    (WS.numels(WS.resnet50()), 25 * MiB),
+    (WS.numels(WS.bert_large()), 25 * MiB),
+    (WS.numels(WS.bert_large()), 0),
+    (WS.numels(WS.bert_large()), 1 * MiB),
+    (WS.numels(WS.bert_large()), 200 * MiB),
+    (WS.numels(WS.bert_base()), 25 * MiB),
+    (WS.numels(WS.mlp()), 25 * MiB),
+    (WS.numels(WS.blog_fine1()), 4 * MiB),
+    (WS.numels(WS.blog_coarse4()), 64 * MiB),
+    ([], 25 * MiB),
+    ([0, 5, 0, 7], 0),
+]
+
+
+@pytest.mark.parametrize("numels,cap", PLAN_CASES)
+def test_plan_and_locators_match_oracle(host, numels, cap):
+    red = _reducer(host, numels, 2, cap)
+    want = OP.compute_bucket_assignment_by_size(numels, 4, cap)
+    assert red.buckets() == want
+    assert red.bucket_bytes() == [4 * x for x in OP.bucket_numels(want, numels)]
+    loc = OP.locators(want, numels)
+    for v in range(len(numels)):
+        assert red.locator(v) == (loc[v].bucket, loc[v].intra, loc[v].offset, loc[v].length)
+
+
+@pytest.mark.parametrize("seed", range(25))
+def test_plan_random_matches_oracle(host, seed):
+    rng = np.random.default_rng(seed)
+    numels = WG.random_numels(seed, int(rng.integers(1, 60)), 0, 20000)
+    cap = int(rng.integers(0, 4 * sum(numels) + 10))
+    red = _reducer(host, numels, 3, cap)
+    assert red.buckets() == OP.compute_bucket_assignment_by_size(numels, 4, cap)
+
+
+@pytest.mark.parametrize("numels,cap", PLAN_CASES[:8])
+def test_segment_table_covers_every_variable_once(host, numels, cap):
+    red = _reducer(host, numels, 2, cap)
+    nseg, seg_elems = host.num_segments(red.h)
+    assert seg_elems >= 64 and seg_elems % 64 == 0
+    buckets = red.buckets()
+    seen = 0
+    for b, members in enumerate(buckets):
+        first, count = host.get_bucket_segments(red.h, b)
+        assert first == seen
+        segs = [host.get_segment(red.h, first + i) for i in range(count)]
+        k = 0
+        for v in members:
+            _, _, off, n = red.locator(v)
+            start = 0
+            while start < n:
+                var, bb, st, ln, bo = segs[k]
+                assert (var, bb, st, bo) == (v, b, start, off + start)
+                assert 0 < ln <= seg_elems and (ln == seg_elems or start + ln == n)
+                start += ln
+                k += 1
+        assert k == count
+        seen += count
+    assert seen == nseg
+    assert nseg == sum((n + seg_elems - 1) // seg_elems for n in numels)
+
+
+def test_workspace_bytes(host):
+    numels = [10, 100, 3]
+    red = _reducer(host, numels, 4, 0)
+    assert red.workspace_bytes(D.MODE_FUSED) == 0
+    # three one-tensor buckets padded to 64 elements each, R + 1 copies
+    assert red.workspace_bytes(D.MODE_STAGED) == (4 + 1) * (64 + 128 + 64) * 4
+
+
+# --- readiness state machine vs the oracle ------------------------------------------
+
+@pytest.mark.parametrize("seed", range(30))
+def test_launch_log_matches_oracle_random_orders(host, seed):
+    rng = np.random.default_rng(100 + seed)
+    P = int(rng.integers(1, 40))
+    numels = WG.random_numels(seed, P, 1, 64)
+    cap = int(rng.integers(0, 4 * sum(numels) // 3 + 1))
+    orc = OR.Reducer(numels, 2, cap)
+    orc.bind([[np.zeros(n, np.float32) for n in numels] for _ in range(2)])
+    red = _reducer(host, numels, 2, cap)
+    _bind_fake(red)
+    for it in range(3):                      # several iterations in a row
+        order = WG.permutation(seed * 10 + it, P)
+        orc.launch_log.clear()
+        orc.sync(order)
+        red.sync(order)
+        assert red.launch_log() == orc.launch_log
+
+
+def test_printed_in_order_sequence_native(host):
+    red = _reducer(host, [4, 4, 4], 2, 0)
+    _bind_fake(red)
+    red.mark_ready(2)
+    assert red.launch_log() == [(0, 0)]
+    red.mark_ready(0)                        # bucket 2 completes first: parked
+    assert red.launch_log() == [(0, 0)]
+    red.mark_ready(1)                        # bucket 1, then the parked bucket 2
+    assert red.launch_log() == [(0, 0), (1, 2), (2, 2)]
+    red.finalize()
+
+
+def test_mark_ready_many_equals_single_calls(host):
+    numels = WG.random_numels(5, 30, 1, 100)
+    order = WG.permutation(5, 30)
+    a, b = _reducer(host, numels, 2, 400), _reducer(host, numels, 2, 400)
+    _bind_fake(a)
+    _bind_fake(b)
+    a.sync(order)
+    b.mark_ready_many(order)
+    b.finalize()
+    assert a.launch_log() == b.launch_log()
+
+
+# --- errors ----------------------------------------------------------------------------
+
+def _code(fn, *a):
+    try:
+        fn(*a)
+    except D.DdpbError as e:
+        return e.code
+    return 0
+
+
+def test_errors(host):
+    red = _reducer(host, [4, 4, 4], 2, 0)
+    assert _code(red.mark_ready, 0) == _abi.E_STATE          # not bound
+    _bind_fake(red)
+    assert _code(red.mark_ready, 3) == _abi.E_INDEX
+    assert _code(red.mark_ready, -1) == _abi.E_INDEX
+    red.mark_ready(2)
+    assert _code(red.mark_ready, 2) == _abi.E_DOUBLE_READY
+    assert _code(red.set_sync, False) == _abi.E_STATE        # mid-iteration
+    red.mark_ready(1)                                        # variable 0 never arrives
+    assert _code(red.finalize) == _abi.E_INCOMPLETE
+    assert "prior iteration" in host.last_error() or "not every bucket" in host.last_error()
+    assert _code(red.mark_ready, 2) == _abi.E_INCOMPLETE     # latched
+    assert _code(red.ensure_prior_reduction_finished) == _abi.E_INCOMPLETE
+    red.reset()
+    red.ensure_prior_reduction_finished()
+    red.sync()
+    assert red.launch_log() == [(0, 0), (1, 1), (2, 2)]
+
+
+def test_unfinished_iteration_detected_before_next_forward(host):
+    red = _reducer(host, [4, 4], 2, 0)
+    _bind_fake(red)
+    red.mark_ready(1)
+    assert _code(red.ensure_prior_reduction_finished) == _abi.E_INCOMPLETE
+    assert "Expected to have finished reduction in the prior iteration" in host.last_error()
+
+
+def test_create_argument_errors(host):
+    assert _code(host.reducer_create, [(4,)], D.F32, 0, 0) == _abi.E_ARG          # R = 0
+    assert _code(host.reducer_create, [(4,)], D.F32, 0, 65) == _abi.E_ARG         # R too large
+    assert _code(host.reducer_create, [(4,)], D.F32, -1, 2) == _abi.E_ARG         # negative cap
+    assert _code(host.reducer_create, [(4,)], D.BF16, 0, 2) == _abi.E_ARG         # fp32 only
+    assert _code(host.reducer_create, [(4, -1)], D.F32, 0, 2) == _abi.E_ARG       # negative dim
+    h = host.reducer_create([(), (2, 3)], D.F32, 0, 2)                             # scalar param
+    assert host.get_locator(h, 0)[3] == 1 and host.get_locator(h, 1)[3] == 6
+    host.destroy(h)
+
+
+def test_bind_argument_errors(host):
+    red = _reducer(host, [4, 4], 2, 0)
+    ptrs = [0x1000] * 4
+    assert _code(red.bind_ptrs, ptrs, 0, 0, 0, []) == _abi.E_ARG                  # no side stream
+    assert _code(red.bind_ptrs, [0] * 4) == _abi.E_ARG                            # null gradient
+    assert _code(red.bind_ptrs, ptrs, 0, 0, 0, [0], 1) == _abi.E_ARG              # staged needs workspace
+    assert _code(red.bind_ptrs, ptrs, 0, 0, 0, [0], 7) == _abi.E_ARG              # bad mode
+    red.bind_ptrs(ptrs)
+    red.mark_ready(1)
+    assert _code(red.bind_ptrs, ptrs) == _abi.E_STATE                             # mid-iteration
+
+
+def test_no_sync_makes_hooks_noops(host):
+    red = _reducer(host, [4, 4, 4], 2, 0)
+    _bind_fake(red)
+    red.set_sync(False)
+    red.sync()                                   # hooks run, nothing launches
+    assert red.launch_log() == []
+    red.finalize()                               # no-op
+    red.set_sync(True)
+    red.sync()
+    assert [b for b, _ in red.launch_log()] == [0, 1, 2]
+
+
+def test_empty_model(host):
+    red = _reducer(host, [], 4, 25 * MiB)
+    assert red.num_buckets == 0
+    red.bind_ptrs([], side_streams=[0])
+    red.finalize()
