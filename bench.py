@@ -46,10 +46,16 @@ def parse():
     ap.add_argument("--config", type=int, default=3, choices=[2, 3, 4, 5])
     ap.add_argument("--cap-mib", type=float, default=None)
     ap.add_argument("--mode", choices=["fused", "staged"], default="fused")
-    ap.add_argument("--n-side", type=int, default=1)
+    ap.add_argument("--n-side", type=int, default=2,
+                    help="side streams; buckets go round-robin over them")
+    ap.add_argument("--launch-blocks", type=int, default=None,
+                    help="cap on workgroups per reduction launch (0 = whole GPU); "
+                         "default 0, and for --config 5 a sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-gb", type=float, default=8.0,
-                    help="algorithmic bytes (2*R*S) of the oracle's timed sample")
+    ap.add_argument("--cpu-sample-gb", type=float, default=24.0,
+                    help="cap on the algorithmic bytes (2*R*S) of the oracle's sample")
+    ap.add_argument("--cpu-min-seconds", type=float, default=10.0,
+                    help="the oracle repeats the sample's sync until this much CPU time")
     ap.add_argument("--no-time-launches", action="store_true",
                     help="do not record per-launch events (roofline becomes null)")
     return ap.parse_args()
@@ -75,6 +81,23 @@ def traffic_from_profiles(kernel: str, workload: str):
     return e.get("bytes_per_launch")
 
 
+def union_length(starts, durs) -> float:
+    """Length of the union of the intervals [s, s + d)."""
+    iv = sorted(zip(starts, durs))
+    total, cur_s, cur_e = 0.0, None, None
+    for s, d in iv:
+        e = s + d
+        if cur_e is None or s > cur_e:
+            if cur_e is not None:
+                total += cur_e - cur_s
+            cur_s, cur_e = s, e
+        else:
+            cur_e = max(cur_e, e)
+    if cur_e is not None:
+        total += cur_e - cur_s
+    return total
+
+
 def hbm_copy_ceiling(torch, gb: float = 2.0) -> float:
     """Plain device-to-device copy bandwidth (read + write bytes / time)."""
     n = int(gb * 1e9 / 4)
@@ -96,7 +119,7 @@ def hbm_copy_ceiling(torch, gb: float = 2.0) -> float:
     return 2 * n * 4 / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline_sync(w, host_in, nvars_sample, sample_bytes):
+def cpu_baseline_sync(w, host_in, nvars_sample, sample_bytes, min_seconds):
     """Times the oracle (plain NumPy, single-threaded) on the first buckets of
     the same workload and inputs."""
     import numpy as np
@@ -108,11 +131,16 @@ def cpu_baseline_sync(w, host_in, nvars_sample, sample_bytes):
     red = OR.Reducer(sub, w.R, w.cap_bytes)
     grads = [[host_in[v][r].copy() for v in range(first_v, P)] for r in range(w.R)]
     red.bind(grads)
+    reps = 0
     t0 = time.perf_counter()
-    red.sync()
-    dt = time.perf_counter() - t0
-    gbs = 2 * w.R * sample_bytes / dt / 1e9
-    return gbs, dt, red.B
+    while True:                      # whole syncs until about min_seconds of CPU work
+        red.sync()
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    gbs = 2 * w.R * sample_bytes * reps / dt / 1e9
+    return gbs, dt, red.B, reps
 
 
 def run_sync_bench(args, torch, D, WG, WC):
@@ -140,8 +168,14 @@ def run_sync_bench(args, torch, D, WG, WC):
     red = D.Reducer([p.shape for p in params], R, w.cap_bytes)
     B = red.num_buckets
     flags = 0 if args.no_time_launches else D.BIND_TIME_LAUNCHES
+    # The compute stream and the side streams are consecutive streams of
+    # torch's pool, so the HIP runtime places them on distinct hardware queues
+    # (it hands out its 4 queues round-robin); the legacy null stream stays idle.
+    compute = torch.cuda.Stream()
     sides = [torch.cuda.Stream() for _ in range(args.n_side)]
-    red.bind(grads, side_streams=sides, mode=mode, flags=flags)
+    torch.cuda.set_stream(compute)
+    red.bind(grads, compute_stream=compute, side_streams=sides, mode=mode, flags=flags)
+    red.set_launch_blocks(args.launch_blocks or 0)
     order = w.ready_order()
 
     # snapshot of the oracle's sample (first buckets), before any sync
@@ -166,21 +200,22 @@ def run_sync_bench(args, torch, D, WG, WC):
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps)")
 
-    compute = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    launch_ms = []
+    per_step = []                       # (starts, durations) of every launch, per step
     torch.cuda.synchronize()            # barrier (one process) + device sync
     t0 = time.perf_counter()
     ev0.record(compute)
     for k in range(args.steps):
         red.sync(order)
         if flags and k >= 1:
-            launch_ms += red.launch_times_ms(1)   # step k-1; step k keeps the GPU busy
+            per_step.append(red.launch_times_ms(1, True))   # step k-1; step k keeps the GPU busy
     ev1.record(compute)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     if flags:
-        launch_ms += red.launch_times_ms(0)
+        per_step.append(red.launch_times_ms(0, True))
+    launch_ms = [d for _, ds in per_step for d in ds]
+    busy_ms = sum(union_length(st, ds) for st, ds in per_step)
     wall_ms = (t1 - t0) * 1e3 / args.steps
     ev_ms = ev0.elapsed_time(ev1) / args.steps
     log(f"timed {args.steps} steps: {wall_ms:.3f} ms/step wall, {ev_ms:.3f} ms/step events")
@@ -194,20 +229,26 @@ def run_sync_bench(args, torch, D, WG, WC):
         assert n_launch == B * args.steps, (n_launch, B, args.steps)
         avg_ms = sum(launch_ms) / n_launch
         bytes_per_launch = alg / B
-        achieved = bytes_per_launch / (avg_ms * 1e-3) / 1e9
+        # With one side stream the launches never overlap and busy time is the
+        # sum of launch durations; with several, launches on different streams
+        # run concurrently and the union of their intervals is the time the
+        # kernel occupied the GPU.
+        achieved = alg * args.steps / (busy_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
                     "traffic": traffic_from_profiles(kernel, w.name),
                     "kernel": kernel, "launches": n_launch, "avg_launch_us": round(avg_ms * 1e3, 2),
-                    "alg_bytes_per_launch": bytes_per_launch}
+                    "alg_bytes_per_launch": bytes_per_launch,
+                    "busy_us_per_step": round(busy_ms * 1e3 / args.steps, 2),
+                    "launch_concurrency": round(sum(launch_ms) / busy_ms, 3)}
 
     if host_in is not None:
         log("timing the oracle on the host sample")
-        gbs, dt, nb = cpu_baseline_sync(w, host_in, nvars_sample, sample_bytes)
+        gbs, dt, nb, reps = cpu_baseline_sync(w, host_in, nvars_sample, sample_bytes, args.cpu_min_seconds)
         cpu = {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
                "sample": f"{w.name}: first {nb} of {B} buckets ({nvars_sample} tensors, "
                          f"{sample_bytes / 1e6:.1f} MB per replica, R={R}) from the same device inputs; "
-                         f"NumPy single thread, {dt:.1f} s"}
+                         f"NumPy single thread, {reps} sync(s) in {dt:.1f} s"}
         del host_in
 
     copy_gbps = hbm_copy_ceiling(torch)
@@ -237,6 +278,180 @@ def run_sync_bench(args, torch, D, WG, WC):
     return out
 
 
+def _pool_streams(torch, n_side):
+    compute = torch.cuda.Stream()
+    sides = [torch.cuda.Stream() for _ in range(n_side)]
+    torch.cuda.set_stream(compute)
+    return compute, sides
+
+
+def run_nosync_bench(args, torch, D, WG, WC):
+    """One step = k micro-steps: k-1 local backward passes accumulate under
+    no_sync, the k-th accumulates with sync on and runs the bucketed sync."""
+    w = WC.BERT_BASE_NOSYNC
+    numels = w.numels()
+    P, R, k = len(numels), w.R, w.micro_steps
+    N = sum(numels)
+    S = 4 * N
+    log(f"workload {w.name}: P={P} R={R} k={k} N={N}")
+    grads = [[torch.zeros(n, dtype=torch.float32, device="cuda") for n in numels] for _ in range(R)]
+    steps = [[[WG.normal(WG.seed_of(4, r, v, t), n, "cuda").to(torch.bfloat16) for v, n in enumerate(numels)]
+              for r in range(R)] for t in range(k)]
+    torch.cuda.synchronize()
+    log("inputs generated on the device")
+    compute, sides = _pool_streams(torch, args.n_side)
+    red = D.Reducer([p.shape for p in w.params()], R, w.cap_bytes)
+    red.bind(grads, compute_stream=compute, side_streams=sides, flags=D.BIND_TIME_LAUNCHES)
+    order = w.ready_order()
+    acc_ms = []
+
+    def one_step(timed):
+        for t in range(k):
+            if t == k - 1:
+                red.set_sync(True)
+            e0 = e1 = None
+            if timed:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(compute)
+            red.no_sync_accumulate(steps[t], first_step=(t == 0))
+            if timed:
+                e1.record(compute)
+                acc_ms.append((t, e0, e1))
+            red.sync(order)                    # hooks: no-ops until the last micro-step
+        red.set_sync(False)
+
+    red.set_sync(False)
+    for _ in range(args.warmup):
+        one_step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_step(True)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    acc_first = [a.elapsed_time(b) for t, a, b in acc_ms if t == 0]
+    acc_rest = [a.elapsed_time(b) for t, a, b in acc_ms if t > 0]
+    sync_ms = sum(red.launch_times_ms(0))
+    alg = R * N * (6 + 10 * (k - 1)) + 2 * R * S
+    value = alg / (wall_ms * 1e-3) / 1e9
+    avg_rest = sum(acc_rest) / len(acc_rest)
+    bytes_rest = 10 * R * N
+    achieved = bytes_rest / (avg_rest * 1e-3) / 1e9
+    return {
+        "metric": f"grad-sync GB/s; ms per optimizer step (k={k} no_sync micro-steps + 1 sync), {w.name}",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "tensors": P, "params": N, "replicas": R, "micro_steps": k,
+                   "step_dtype": "bf16", "buckets": red.num_buckets, "alg_bytes_per_step": alg},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "accumulate_first_ms": round(sum(acc_first) / len(acc_first), 4),
+        "accumulate_ms": round(avg_rest, 4), "sync_kernel_ms_last": round(sync_ms, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "accumulate_kernel<bf16,add>", "alg_bytes_per_launch": bytes_rest,
+                     "avg_launch_us": round(avg_rest * 1e3, 2)},
+        "cpu_baseline": None,
+    }
+
+
+def run_overlap_bench(args, torch, D, WG, WC):
+    """Bucketed sync on side streams overlapping a synthetic bf16 backward of a
+    24-layer MLP (d 2048, FFN 8192, 8192 tokens) on the compute stream, which
+    writes replica 0's fp32 gradients layer by layer; replicas 1..7 are
+    resident."""
+    w = WC.MLP_OVERLAP
+    params = w.params()
+    numels = w.numels()
+    P, R = len(numels), w.R
+    S = 4 * sum(numels)
+    L, d, f, T = 24, 2048, 8192, 8192
+    cap = w.cap_bytes if args.cap_mib is None else int(args.cap_mib * MiB)
+    log(f"workload {w.name}: P={P} R={R} S={S / 1e6:.1f} MB cap={cap}")
+    grads = [[torch.empty(n, dtype=torch.float32, device="cuda") for n in numels] for _ in range(R)]
+    for r in range(1, R):
+        for v, n in enumerate(numels):
+            WG.normal(WG.seed_of(5, r, v), n, "cuda", out=grads[r][v])
+    g = torch.Generator(device="cuda").manual_seed(5)
+    bf = torch.bfloat16
+    X = [torch.randn(T, d, device="cuda", dtype=bf, generator=g) for _ in range(L)]
+    H = [torch.randn(T, f, device="cuda", dtype=bf, generator=g) for _ in range(L)]
+    W1 = [torch.randn(f, d, device="cuda", dtype=bf, generator=g) * 0.02 for _ in range(L)]
+    W2 = [torch.randn(d, f, device="cuda", dtype=bf, generator=g) * 0.02 for _ in range(L)]
+    dY0 = torch.randn(T, d, device="cuda", dtype=bf, generator=g)
+    torch.cuda.synchronize()
+    log("inputs generated on the device")
+    compute, sides = _pool_streams(torch, args.n_side)
+    red = D.Reducer([p.shape for p in params], R, cap)
+    red.bind(grads, compute_stream=compute, side_streams=sides, flags=D.BIND_TIME_LAUNCHES)
+    g0 = [grads[0][v].view(params[v].shape) for v in range(P)]
+    order = w.ready_order()
+
+    def backward(hook):
+        dY = dY0
+        for l in range(L - 1, -1, -1):
+            vW1, vb1, vW2, vb2 = 4 * l, 4 * l + 1, 4 * l + 2, 4 * l + 3
+            torch.sum(dY, dim=0, dtype=torch.float32, out=g0[vb2])
+            hook(vb2)
+            torch.mm(dY.t(), H[l], torch.float32, out=g0[vW2])
+            hook(vW2)
+            dH = torch.mm(dY, W2[l])
+            torch.sum(dH, dim=0, dtype=torch.float32, out=g0[vb1])
+            hook(vb1)
+            torch.mm(dH.t(), X[l], torch.float32, out=g0[vW1])
+            hook(vW1)
+            dY = torch.mm(dH, W1[l])
+
+    def none(v):
+        pass
+
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(compute)
+        for _ in range(reps):
+            fn()
+        e1.record(compute)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def both():
+        backward(red.mark_ready)
+        red.finalize()
+
+    t_bwd = timed(lambda: backward(none), args.steps)
+    flops = 4 * 2 * T * d * f * L
+    alg = 2 * R * S
+    sweep = {}
+    caps = [args.launch_blocks] if args.launch_blocks is not None else [0, 16, 32, 64, 128]
+    for mb in caps:
+        red.set_launch_blocks(mb)
+        t_red = timed(lambda: red.sync(order), args.steps)
+        t_both = timed(both, args.steps)
+        hidden = max(0.0, min(1.0, (t_bwd + t_red - t_both) / t_red))
+        sweep[mb] = {"t_reduction_ms": round(t_red, 4), "t_both_ms": round(t_both, 4),
+                     "hidden": round(hidden, 4),
+                     "reduction_kernel_ms_in_overlap": round(sum(red.launch_times_ms(0)), 4)}
+        log(f"launch_blocks={mb}: reduction {t_red:.3f} ms alone, both {t_both:.3f} ms, hidden {hidden:.3f}")
+    best = min(sweep, key=lambda k: sweep[k]["t_both_ms"])
+    b = sweep[best]
+    return {
+        "metric": f"fraction of reduction hidden under backward; ms per step, {w.name}",
+        "value": b["hidden"], "unit": "fraction", "n_gpus": 1, "steps": args.steps, "warmup": 2,
+        "ms_per_step": b["t_both_ms"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 GEMM / f32 reduce", "data": "synthetic",
+        "config": {"workload": w.name, "tensors": P, "replicas": R, "bucket_cap_bytes": cap,
+                   "buckets": red.num_buckets, "tokens": T, "side_streams": args.n_side, "launch_blocks": best},
+        "t_backward_ms": round(t_bwd, 4), "t_reduction_ms": b["t_reduction_ms"], "t_both_ms": b["t_both_ms"],
+        "backward_TFLOPs": round(flops / (t_bwd * 1e-3) / 1e12, 1),
+        "reduction_GBps": round(alg / (b["t_reduction_ms"] * 1e-3) / 1e9, 1),
+        "launch_blocks_sweep": sweep,
+        "roofline": None, "cpu_baseline": None,
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -254,10 +469,8 @@ def main():
     if args.config in (2, 3):
         out = run_sync_bench(args, torch, D, WG, WC)
     elif args.config == 4:
-        from bench_extra import run_nosync_bench
         out = run_nosync_bench(args, torch, D, WG, WC)
     else:
-        from bench_extra import run_overlap_bench
         out = run_overlap_bench(args, torch, D, WG, WC)
     print(json.dumps(out), flush=True)
 

@@ -28,7 +28,7 @@ SYMBOLS = [
     "ddpb_num_segments", "ddpb_get_bucket_segments", "ddpb_get_segment", "ddpb_workspace_bytes",
     "ddpb_bind", "ddpb_ensure_prior_reduction_finished", "ddpb_mark_ready", "ddpb_mark_ready_many",
     "ddpb_finalize", "ddpb_set_sync", "ddpb_no_sync_accumulate", "ddpb_reset", "ddpb_get_launch_log",
-    "ddpb_get_launch_times", "ddpb_device_clock_hz", "ddpb_last_error",
+    "ddpb_get_launch_times", "ddpb_device_clock_hz", "ddpb_last_error", "ddpb_set_launch_blocks",
 ]
 
 
@@ -62,8 +62,9 @@ def _sig(lib):
         "ddpb_no_sync_accumulate": [vp, C.POINTER(vp), i32, i32],
         "ddpb_reset": [vp],
         "ddpb_get_launch_log": [vp, P32, P32, P64, P64, i32, P32],
-        "ddpb_get_launch_times": [vp, i32, C.POINTER(C.c_float), i32, P32],
+        "ddpb_get_launch_times": [vp, i32, C.POINTER(C.c_float), C.POINTER(C.c_float), i32, P32],
         "ddpb_device_clock_hz": [vp, P64],
+        "ddpb_set_launch_blocks": [vp, i32],
         "ddpb_last_error": [],
     }
     for name, args in S.items():
@@ -191,12 +192,20 @@ class Lib:
             return rows, [t0[i] for i in range(m)], [t1[i] for i in range(m)]
         return rows
 
-    def get_launch_times(self, h, iterations_ago: int = 0) -> List[float]:
+    def get_launch_times(self, h, iterations_ago: int = 0, with_starts: bool = False):
+        """Durations (ms) of each launch of a finalized iteration; with
+        ``with_starts`` also their starts relative to its first launch."""
         n = i32()
-        self._check(self.dll.ddpb_get_launch_times(h, iterations_ago, None, 0, C.byref(n)))
+        self._check(self.dll.ddpb_get_launch_times(h, iterations_ago, None, None, 0, C.byref(n)))
         arr = (C.c_float * max(n.value, 1))()
-        self._check(self.dll.ddpb_get_launch_times(h, iterations_ago, arr, n.value, C.byref(n)))
+        st = (C.c_float * max(n.value, 1))()
+        self._check(self.dll.ddpb_get_launch_times(h, iterations_ago, st, arr, n.value, C.byref(n)))
+        if with_starts:
+            return list(st[:n.value]), list(arr[:n.value])
         return list(arr[:n.value])
+
+    def set_launch_blocks(self, h, max_blocks: int):
+        self._check(self.dll.ddpb_set_launch_blocks(h, int(max_blocks)))
 
     def device_clock_hz(self, h) -> int:
         hz = i64()

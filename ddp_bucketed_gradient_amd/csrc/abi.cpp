@@ -229,7 +229,8 @@ int ddpb_get_launch_log(ddpb_t h, int32_t* buckets, int32_t* trigger_call, int64
   return DDPB_OK;
 }
 
-int ddpb_get_launch_times(ddpb_t h, int32_t iterations_ago, float* ms, int32_t cap, int32_t* n) {
+int ddpb_get_launch_times(ddpb_t h, int32_t iterations_ago, float* start_ms, float* ms, int32_t cap,
+                          int32_t* n) {
   if (!h || !n || cap < 0 || (cap > 0 && !ms)) return fail(DDPB_E_ARG, "get_launch_times: bad argument");
   const int64_t fin = h->red.finalized();
   if (iterations_ago < 0 || iterations_ago >= ddpb::kTimeRing || iterations_ago >= fin)
@@ -240,11 +241,20 @@ int ddpb_get_launch_times(ddpb_t h, int32_t iterations_ago, float* ms, int32_t c
   const int32_t m = std::min<int32_t>(cap, *n);
   if (m == 0) return DDPB_OK;
   std::vector<ddpb::LaunchRecord> part(log.begin(), log.begin() + m);
-  std::vector<float> t;
+  std::vector<float> st, t;
   std::string err;
-  const int rc = h->red.launcher()->read_times(it, part, &t, &err);
+  const int rc = h->red.launcher()->read_times(it, part, &st, &t, &err);
   if (rc != DDPB_OK) return fail(rc, err);
-  for (int32_t i = 0; i < m; ++i) ms[i] = t[i];
+  for (int32_t i = 0; i < m; ++i) {
+    ms[i] = t[i];
+    if (start_ms) start_ms[i] = st[i];
+  }
+  return DDPB_OK;
+}
+
+int ddpb_set_launch_blocks(ddpb_t h, int32_t max_blocks) {
+  if (!h || max_blocks < 0) return fail(DDPB_E_ARG, "set_launch_blocks: bad argument");
+  h->red.launcher()->set_max_blocks(max_blocks);
   return DDPB_OK;
 }
 

@@ -108,10 +108,13 @@ class Launcher {
   // Device clock stamps of the given launched buckets (zeros when disabled).
   virtual int read_stamps(const std::vector<LaunchRecord>& log, std::vector<int64_t>* t0,
                           std::vector<int64_t>* t1, std::string* err) = 0;
-  // Waits for, then returns, the kernel time of each launch of `iteration`.
-  virtual int read_times(int64_t iteration, const std::vector<LaunchRecord>& log, std::vector<float>* ms,
-                         std::string* err) = 0;
+  // Waits for, then returns, the start (relative to the iteration's first
+  // launch) and the duration of each launch of `iteration`, in milliseconds.
+  virtual int read_times(int64_t iteration, const std::vector<LaunchRecord>& log, std::vector<float>* start_ms,
+                         std::vector<float>* ms, std::string* err) = 0;
   virtual int clock_hz(int64_t* hz, std::string* err) = 0;
+  // Caps the workgroups of each reduction launch (0 = one per four segments).
+  virtual void set_max_blocks(int32_t n) = 0;
 };
 
 std::unique_ptr<Launcher> make_launcher();

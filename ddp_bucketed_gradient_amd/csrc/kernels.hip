@@ -26,6 +26,7 @@
 //   accumulate_kernel   no_sync: grad (+)= float(step) for every replica.
 //
 // Short page names are defined in core.hpp.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -69,6 +70,11 @@ __device__ __forceinline__ gfloat* G(float* p) { return (gfloat*)p; }
 __device__ __forceinline__ const gfloat* G(const float* p) { return (const gfloat*)p; }
 __device__ __forceinline__ v4f ld4(const float* p) { return *(const gv4f*)p; }
 __device__ __forceinline__ void st4(float* p, v4f v) { *(gv4f*)p = v; }
+// Streaming variants: every gradient byte is touched exactly once per launch,
+// so the data are marked non-temporal and do not displace other kernels'
+// working sets in L2 and the Infinity Cache.
+__device__ __forceinline__ v4f ld4s(const float* p) { return __builtin_nontemporal_load((const gv4f*)p); }
+__device__ __forceinline__ void st4s(float* p, v4f v) { __builtin_nontemporal_store(v, (gv4f*)p); }
 
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(1))) v2u gv2u;
@@ -138,8 +144,9 @@ __global__ __launch_bounds__(kBlock) void fused_mean_kernel(const Segment* __res
                                                             int64_t* __restrict__ stamp) {
   constexpr int U = Unroll<R>::value;
   stamp_begin(stamp);
-  const int s = blockIdx.x * kWavesPerBlock + wave_id();
-  if (s < nseg) {
+  // One wavefront per segment; with a capped grid (fewer workgroups than
+  // segments / 4) each wavefront strides over the remaining segments.
+  for (int s = blockIdx.x * kWavesPerBlock + wave_id(); s < nseg; s += gridDim.x * kWavesPerBlock) {
     const Segment g = segs[s];
     const int len = static_cast<int>(g.len);
     float* p[R];
@@ -155,7 +162,7 @@ __global__ __launch_bounds__(kBlock) void fused_mean_kernel(const Segment* __res
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
-          for (int r = 0; r < R; ++r) x[u][r] = ld4(p[r] + 4 * (i + 64 * u));
+          for (int r = 0; r < R; ++r) x[u][r] = ld4s(p[r] + 4 * (i + 64 * u));
         // Keep all U*R loads in flight: the scheduler may not sink them
         // between the adds (it would otherwise trade bandwidth for registers).
         __builtin_amdgcn_sched_barrier(0);
@@ -163,16 +170,16 @@ __global__ __launch_bounds__(kBlock) void fused_mean_kernel(const Segment* __res
         for (int u = 0; u < U; ++u) {
           const v4f m = mean4<R>(x[u], scale);
 #pragma unroll
-          for (int r = 0; r < R; ++r) st4(p[r] + 4 * (i + 64 * u), m);
+          for (int r = 0; r < R; ++r) st4s(p[r] + 4 * (i + 64 * u), m);
         }
       }
       for (; i < n4; i += 64) {
         v4f x[R];
 #pragma unroll
-        for (int r = 0; r < R; ++r) x[r] = ld4(p[r] + 4 * i);
+        for (int r = 0; r < R; ++r) x[r] = ld4s(p[r] + 4 * i);
         const v4f m = mean4<R>(x, scale);
 #pragma unroll
-        for (int r = 0; r < R; ++r) st4(p[r] + 4 * i, m);
+        for (int r = 0; r < R; ++r) st4s(p[r] + 4 * i, m);
       }
       tail = n4 * 4;
     }
@@ -197,8 +204,9 @@ __global__ __launch_bounds__(kBlock) void fused_mean_kernel_rt(const Segment* __
                                                                int32_t R, float scale, int32_t pow2,
                                                                int64_t* __restrict__ stamp) {
   stamp_begin(stamp);
-  const int s = blockIdx.x * kWavesPerBlock + wave_id();
-  if (s < nseg) {
+  // One wavefront per segment; with a capped grid (fewer workgroups than
+  // segments / 4) each wavefront strides over the remaining segments.
+  for (int s = blockIdx.x * kWavesPerBlock + wave_id(); s < nseg; s += gridDim.x * kWavesPerBlock) {
     const Segment g = segs[s];
     const int len = static_cast<int>(g.len);
     for (int j = lane_id(); j < len; j += 64) {
@@ -221,8 +229,9 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(const Segment* __restrict_
                                                       float* __restrict__ flat, int64_t flat_stride,
                                                       int64_t fbase, int32_t vec_ok, int64_t* __restrict__ stamp) {
   stamp_begin(stamp);
-  const int s = blockIdx.x * kWavesPerBlock + wave_id();
-  if (s < nseg) {
+  // One wavefront per segment; with a capped grid (fewer workgroups than
+  // segments / 4) each wavefront strides over the remaining segments.
+  for (int s = blockIdx.x * kWavesPerBlock + wave_id(); s < nseg; s += gridDim.x * kWavesPerBlock) {
     const Segment g = segs[s];
     const int len = static_cast<int>(g.len);
     const int lane = lane_id();
@@ -289,8 +298,9 @@ __global__ __launch_bounds__(kBlock) void copyback_kernel(const Segment* __restr
                                                           const float* __restrict__ avg, int64_t fbase,
                                                           int32_t vec_ok, int64_t* __restrict__ stamp) {
   stamp_begin(stamp);
-  const int s = blockIdx.x * kWavesPerBlock + wave_id();
-  if (s < nseg) {
+  // One wavefront per segment; with a capped grid (fewer workgroups than
+  // segments / 4) each wavefront strides over the remaining segments.
+  for (int s = blockIdx.x * kWavesPerBlock + wave_id(); s < nseg; s += gridDim.x * kWavesPerBlock) {
     const Segment g = segs[s];
     const int len = static_cast<int>(g.len);
     const int lane = lane_id();
@@ -494,10 +504,12 @@ class HipLauncher final : public Launcher {
         waited |= 1u << si;
       }
       side_used_[si] = 1;
-      if (flags_ & 2) HIP_OK(hipEventRecord(ev_t0_[ring + b], s), "hipEventRecord(t0)");
-      const int rc = enqueue_bucket(b, s, err);
+      // Timing events ride on the kernel dispatches themselves (start of the
+      // bucket's first kernel, end of its last), not on separate markers.
+      hipEvent_t t0 = (flags_ & 2) ? ev_t0_[ring + b] : nullptr;
+      hipEvent_t t1 = (flags_ & 2) ? ev_t1_[ring + b] : nullptr;
+      const int rc = enqueue_bucket(b, s, t0, t1, err);
       if (rc != kOk) return rc;
-      if (flags_ & 2) HIP_OK(hipEventRecord(ev_t1_[ring + b], s), "hipEventRecord(t1)");
     }
     return kOk;
   }
@@ -578,21 +590,27 @@ class HipLauncher final : public Launcher {
     return kOk;
   }
 
-  int read_times(int64_t iteration, const std::vector<LaunchRecord>& log, std::vector<float>* ms,
-                 std::string* err) override {
+  int read_times(int64_t iteration, const std::vector<LaunchRecord>& log, std::vector<float>* start_ms,
+                 std::vector<float>* ms, std::string* err) override {
     if (!(flags_ & 2)) {
       *err = "launch timing was not enabled at bind";
       return kErrState;
     }
     const size_t ring = static_cast<size_t>(iteration % kTimeRing) * plan_->B();
     ms->resize(log.size());
+    start_ms->resize(log.size());
+    if (log.empty()) return kOk;
+    const hipEvent_t ref = ev_t0_[ring + static_cast<size_t>(log[0].bucket)];
     for (size_t i = 0; i < log.size(); ++i) {
       const size_t b = ring + static_cast<size_t>(log[i].bucket);
       HIP_OK(hipEventSynchronize(ev_t1_[b]), "hipEventSynchronize(t1)");
       HIP_OK(hipEventElapsedTime(&(*ms)[i], ev_t0_[b], ev_t1_[b]), "hipEventElapsedTime");
+      HIP_OK(hipEventElapsedTime(&(*start_ms)[i], ref, ev_t0_[b]), "hipEventElapsedTime");
     }
     return kOk;
   }
+
+  void set_max_blocks(int32_t n) override { max_blocks_ = n; }
 
   int clock_hz(int64_t* hz, std::string* err) override {
     int dev = 0, khz = 0;
@@ -603,20 +621,26 @@ class HipLauncher final : public Launcher {
   }
 
  private:
-  int enqueue_bucket(int32_t b, hipStream_t s, std::string* err) {
+  int enqueue_bucket(int32_t b, hipStream_t s, hipEvent_t t0, hipEvent_t t1, std::string* err) {
     const int32_t s0 = plan_->seg_first[b];
     const int32_t nseg = plan_->seg_first[b + 1] - s0;
-    if (nseg == 0) return kOk;                 // bucket of empty tensors
+    if (nseg == 0) {                          // bucket of empty tensors: nothing to move
+      if (t0) HIP_OK(hipEventRecord(t0, s), "hipEventRecord(t0)");
+      if (t1) HIP_OK(hipEventRecord(t1, s), "hipEventRecord(t1)");
+      return kOk;
+    }
     const Segment* segs = d_segs_ + s0;
     int64_t* stamp = (flags_ & 1) ? d_stamps_ + static_cast<int64_t>(b) * 4 : nullptr;
-    const dim3 grid(static_cast<unsigned>((nseg + kWavesPerBlock - 1) / kWavesPerBlock));
+    int64_t blocks = (nseg + kWavesPerBlock - 1) / kWavesPerBlock;
+    if (max_blocks_ > 0) blocks = std::min<int64_t>(blocks, max_blocks_);
+    const dim3 grid(static_cast<unsigned>(blocks));
     const dim3 block(kBlock);
     if (mode_ == 0) {
       switch (R_) {
-#define DDPB_FUSED_CASE(RR)                                                                               \
-  case RR:                                                                                                \
-    hipLaunchKernelGGL((fused_mean_kernel<RR>), grid, block, 0, s, segs, nseg, d_grads_, P_, scale_, vec_ok_, \
-                       stamp);                                                                            \
+#define DDPB_FUSED_CASE(RR)                                                                                      \
+  case RR:                                                                                                       \
+    hipExtLaunchKernelGGL((fused_mean_kernel<RR>), grid, block, 0, s, t0, t1, 0, segs, nseg, d_grads_, P_, scale_, \
+                          vec_ok_, stamp);                                                                       \
     break;
         DDPB_FUSED_CASE(1) DDPB_FUSED_CASE(2) DDPB_FUSED_CASE(3) DDPB_FUSED_CASE(4)
         DDPB_FUSED_CASE(5) DDPB_FUSED_CASE(6) DDPB_FUSED_CASE(7) DDPB_FUSED_CASE(8)
@@ -624,8 +648,8 @@ class HipLauncher final : public Launcher {
         DDPB_FUSED_CASE(13) DDPB_FUSED_CASE(14) DDPB_FUSED_CASE(15) DDPB_FUSED_CASE(16)
 #undef DDPB_FUSED_CASE
         default:
-          hipLaunchKernelGGL(fused_mean_kernel_rt, grid, block, 0, s, segs, nseg, d_grads_, P_, R_, scale_,
-                             pow2_ ? 1 : 0, stamp);
+          hipExtLaunchKernelGGL(fused_mean_kernel_rt, grid, block, 0, s, t0, t1, 0, segs, nseg, d_grads_, P_, R_,
+                                scale_, pow2_ ? 1 : 0, stamp);
       }
       HIP_OK(hipGetLastError(), "launch fused_mean_kernel");
       return kOk;
@@ -634,11 +658,13 @@ class HipLauncher final : public Launcher {
     const int64_t fbase = plan_->flat_base[b];
     const int64_t n = plan_->bucket_elems[b];
     const int64_t stride = plan_->flat_elems;
-    hipLaunchKernelGGL(pack_kernel, grid, block, 0, s, segs, nseg, d_grads_, P_, R_, flat_, stride, fbase, vec_ok_,
-                       stamp);
+    hipExtLaunchKernelGGL(pack_kernel, grid, block, 0, s, t0, nullptr, 0, segs, nseg, d_grads_, P_, R_, flat_, stride,
+                          fbase, vec_ok_, stamp);
     HIP_OK(hipGetLastError(), "launch pack_kernel");
     const int64_t n4 = std::max<int64_t>(n >> 2, 1);
-    const dim3 mgrid(static_cast<unsigned>(std::min<int64_t>((n4 + kBlock - 1) / kBlock, 2048)));
+    int64_t mblocks = std::min<int64_t>((n4 + kBlock - 1) / kBlock, 2048);
+    if (max_blocks_ > 0) mblocks = std::min<int64_t>(mblocks, max_blocks_);
+    const dim3 mgrid(static_cast<unsigned>(mblocks));
     switch (R_) {
 #define DDPB_MEAN_CASE(RR)                                                                                   \
   case RR:                                                                                                   \
@@ -654,8 +680,8 @@ class HipLauncher final : public Launcher {
                            pow2_ ? 1 : 0, nullptr);
     }
     HIP_OK(hipGetLastError(), "launch mean_kernel");
-    hipLaunchKernelGGL(copyback_kernel, grid, block, 0, s, segs, nseg, d_grads_, P_, R_, avg_, fbase, vec_ok_,
-                       nullptr);
+    hipExtLaunchKernelGGL(copyback_kernel, grid, block, 0, s, nullptr, t1, 0, segs, nseg, d_grads_, P_, R_, avg_,
+                          fbase, vec_ok_, static_cast<int64_t*>(nullptr));
     HIP_OK(hipGetLastError(), "launch copyback_kernel");
     return kOk;
   }
@@ -689,6 +715,7 @@ class HipLauncher final : public Launcher {
   bool pow2_ = true;
   float scale_ = 1.0f;
   int32_t vec_ok_ = 1;
+  int32_t max_blocks_ = 0;     // cap on workgroups per reduction launch (0 = none)
   hipStream_t compute_ = nullptr;
   std::vector<hipStream_t> side_;
   std::vector<uint8_t> side_used_;

@@ -19,10 +19,12 @@ class NullLauncher final : public Launcher {
     t1->assign(log.size(), 0);
     return kOk;
   }
-  int read_times(int64_t, const std::vector<LaunchRecord>&, std::vector<float>*, std::string* err) override {
+  int read_times(int64_t, const std::vector<LaunchRecord>&, std::vector<float>*, std::vector<float>*,
+                 std::string* err) override {
     *err = "no device in the host-only test build";
     return kErrState;
   }
+  void set_max_blocks(int32_t) override {}
   int clock_hz(int64_t* hz, std::string*) override {
     *hz = 0;
     return kOk;

@@ -127,8 +127,12 @@ class Reducer:
     def launch_log(self, with_stamps: bool = False):
         return self.lib.get_launch_log(self.h, with_stamps)
 
-    def launch_times_ms(self, iterations_ago: int = 0) -> List[float]:
-        return self.lib.get_launch_times(self.h, iterations_ago)
+    def launch_times_ms(self, iterations_ago: int = 0, with_starts: bool = False):
+        return self.lib.get_launch_times(self.h, iterations_ago, with_starts)
+
+    def set_launch_blocks(self, max_blocks: int):
+        """Cap the workgroups per reduction launch (0 = whole GPU)."""
+        self.lib.set_launch_blocks(self.h, max_blocks)
 
     def device_clock_hz(self) -> int:
         return self.lib.device_clock_hz(self.h)

@@ -138,6 +138,15 @@ int ddpb_bind(ddpb_t h, void* const* grad_ptrs, void* workspace, int64_t ws_byte
               void* compute_stream, void* const* side_streams, int32_t n_side,
               int32_t mode, int32_t flags);
 
+/* Caps the number of workgroups (256 threads each) of every reduction launch;
+ * 0 (the default) launches one workgroup per four segments, so a bucket uses
+ * the whole GPU. A small cap keeps the reduction on a few compute units while
+ * backward GEMMs keep the rest, the way a collective library restricts itself
+ * to a few channels ([PDTI] §3.1 on collectives occupying compute units).
+ * Each wavefront then strides over the bucket's segments; results do not
+ * depend on the cap. May be called at any time; applies to later launches. */
+int ddpb_set_launch_blocks(ddpb_t h, int32_t max_blocks);
+
 /* ---------------------------------------------------------------------------
  * One iteration ([Li] "Overlapping Computation with Communication";
  * [C30] "Bucket 必须按序发起", "Finalize Backward 与梯度可见性").
@@ -203,13 +212,17 @@ int ddpb_reset(ddpb_t h);
 int ddpb_get_launch_log(ddpb_t h, int32_t* buckets, int32_t* trigger_call,
                         int64_t* dev_t0, int64_t* dev_t1, int32_t cap, int32_t* n);
 
-/* With DDPB_BIND_TIME_LAUNCHES: milliseconds between the events recorded
- * before and after each launched bucket's kernels on its side stream, in
- * launch order, for the finalized iteration `iterations_ago` back (0 = the
- * last one; events of the last 4 iterations are kept, else DDPB_E_INDEX).
+/* With DDPB_BIND_TIME_LAUNCHES: per launched bucket, in launch order, for the
+ * finalized iteration `iterations_ago` back (0 = the last one; the last 4
+ * iterations are kept, else DDPB_E_INDEX):
+ *   ms[i]        duration from the start of the bucket's first kernel to the
+ *                end of its last kernel (hipEvents attached to the dispatches)
+ *   start_ms[i]  (may be NULL) start relative to the iteration's first launch,
+ *                so overlapping launches on several side streams can be merged
  * Blocks the host until those events have completed; later iterations may
  * keep running on the device meanwhile. */
-int ddpb_get_launch_times(ddpb_t h, int32_t iterations_ago, float* ms, int32_t cap, int32_t* n);
+int ddpb_get_launch_times(ddpb_t h, int32_t iterations_ago, float* start_ms, float* ms, int32_t cap,
+                          int32_t* n);
 
 /* Device clock rate of wall_clock64 in Hz (for converting launch-log ticks). */
 int ddpb_device_clock_hz(ddpb_t h, int64_t* hz);
