@@ -62,9 +62,13 @@ def parse():
 
 
 def kernel_source_hash() -> str:
-    p = os.path.join(ROOT, "ddp_bucketed_gradient_amd", "csrc", "kernels.hip")
-    with open(p, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256 prefix of the sources that decide what the kernels read and
+    write (kernels, segment planner)."""
+    h = hashlib.sha256()
+    for name in ("kernels.hip", "core.hpp", "core.cpp"):
+        with open(os.path.join(ROOT, "ddp_bucketed_gradient_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profiles(kernel: str, workload: str):

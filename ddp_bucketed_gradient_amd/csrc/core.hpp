@@ -19,8 +19,10 @@
 
 namespace ddpb {
 
-// Elements per device segment: one wavefront processes one segment.
-constexpr int64_t kSegElems = 4096;
+// Elements per device segment: one wavefront processes one segment (32 KiB per
+// replica). Measured on BERT-large shapes, R = 8, two side streams:
+// 2048 / 4096 / 8192 / 16384 elements -> 4.95 / 5.40 / 5.49 / 5.38 TB/s.
+constexpr int64_t kSegElems = 8192;
 // Flat-bucket bases in the staged workspace are padded to this many elements.
 constexpr int64_t kFlatAlignElems = 64;
 constexpr int kMaxReplicas = 64;

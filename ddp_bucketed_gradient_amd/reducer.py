@@ -7,6 +7,7 @@ out while side-stream kernels still use it.
 """
 from __future__ import annotations
 
+import sys as _sys
 from typing import List, Optional, Sequence
 
 from . import _abi
@@ -64,7 +65,9 @@ class Reducer:
         if dev is None:
             dev = torch.device("cuda", torch.cuda.current_device())
         compute = compute_stream if compute_stream is not None else torch.cuda.current_stream(dev)
-        sides = list(side_streams) if side_streams else [torch.cuda.Stream(device=dev)]
+        # default: two side streams, buckets alternate between them so that
+        # consecutive bucket kernels overlap each other's start-up and drain
+        sides = list(side_streams) if side_streams else [torch.cuda.Stream(device=dev) for _ in range(2)]
         nbytes = self.lib.workspace_bytes(self.h, mode)
         ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
         self._keep = [grads, ws, compute, sides]
@@ -144,10 +147,9 @@ class Reducer:
             self._keep = []
 
     def __del__(self):
-        import sys
-        if sys.is_finalizing():      # the HIP runtime may already be gone
-            return
         try:
+            if _sys.is_finalizing():     # the HIP runtime may already be gone
+                return
             self.close()
-        except Exception:
+        except BaseException:
             pass

@@ -399,3 +399,96 @@ def test_config4_bert_base_nosync_sampled():
     for v in sample:
         want = _oracle_nosync_one(hs[v], R, k)
         assert_bits_equal(grads[R - 1][v].cpu().numpy(), want[0], f"v={v}")
+
+
+@pytest.mark.parametrize("mode", [D.MODE_FUSED, D.MODE_STAGED])
+@pytest.mark.parametrize("blocks", [1, 3])
+def test_capped_grid_parity(mode, blocks):
+    """With the workgroups of each launch capped, every wavefront strides over
+    several segments; the result must not change."""
+    numels = RAGGED + [70000, 3, 131072]
+    R = 8
+    order = WG.permutation(77, len(numels))
+    red = D.Reducer([(n,) for n in numels], R, 4 * 30000)
+    red.set_launch_blocks(blocks)
+    grads = alloc_grads(numels, R)
+    red.bind(grads, mode=mode)
+    host = _host_inputs(40 + blocks, numels, R)
+    fill_from_host(grads, host)
+    red.sync(order)
+    got = snapshot(grads)
+    want, log = _oracle_sync(numels, R, 4 * 30000, host, order)
+    assert red.launch_log() == log
+    for v in range(len(numels)):
+        for r in range(R):
+            assert_bits_equal(got[v][r], want[r][v], f"blocks={blocks} v={v} r={r}")
+
+
+def _mlp_backward(params, g0, X, H, W1, W2, dY0, hook):
+    """Backward of [Linear(d, f), Linear(f, d)] blocks in bf16, last layer
+    first; fp32 gradients of replica 0 are written in place."""
+    L = len(X)
+    dY = dY0
+    for l in range(L - 1, -1, -1):
+        vW1, vb1, vW2, vb2 = 4 * l, 4 * l + 1, 4 * l + 2, 4 * l + 3
+        torch.sum(dY, dim=0, dtype=torch.float32, out=g0[vb2])
+        hook(vb2)
+        torch.mm(dY.t(), H[l], torch.float32, out=g0[vW2])
+        hook(vW2)
+        dH = torch.mm(dY, W2[l])
+        torch.sum(dH, dim=0, dtype=torch.float32, out=g0[vb1])
+        hook(vb1)
+        torch.mm(dH.t(), X[l], torch.float32, out=g0[vW1])
+        hook(vW1)
+        dY = torch.mm(dH, W1[l])
+
+
+@pytest.mark.parametrize("size", ["small", "full"])
+def test_config5_overlap_parity(size):
+    """Replica 0's gradients come from a bf16 backward on the compute stream,
+    layer by layer, each hook right after its gradient is written; buckets are
+    reduced on two side streams meanwhile."""
+    if size == "small":
+        L, d, f, T, cap = 3, 256, 1024, 512, 4 * 300000
+        sample = None
+    else:
+        L, d, f, T, cap = 24, 2048, 8192, 8192, WC.MLP_OVERLAP.cap_bytes
+        sample = {95, 94, 93, 92, 1, 0}
+    params = WS.mlp(L, d, f)
+    numels = WS.numels(params)
+    P, R = len(numels), 8
+    say(f"config5 {size}: L={L} d={d} f={f} T={T} P={P}")
+    comp = torch.cuda.Stream()
+    sides = [torch.cuda.Stream(), torch.cuda.Stream()]
+    with torch.cuda.stream(comp):
+        grads = alloc_grads(numels, R)
+        for r in range(1, R):
+            for v, n in enumerate(numels):
+                WG.normal(WG.seed_of(5, r, v), n, "cuda", out=grads[r][v])
+        g = torch.Generator(device="cuda").manual_seed(5)
+        bf = torch.bfloat16
+        X = [torch.randn(T, d, device="cuda", dtype=bf, generator=g) for _ in range(L)]
+        H = [torch.randn(T, f, device="cuda", dtype=bf, generator=g) for _ in range(L)]
+        W1 = [torch.randn(f, d, device="cuda", dtype=bf, generator=g) * 0.02 for _ in range(L)]
+        W2 = [torch.randn(d, f, device="cuda", dtype=bf, generator=g) * 0.02 for _ in range(L)]
+        dY0 = torch.randn(T, d, device="cuda", dtype=bf, generator=g)
+        red = D.Reducer([p.shape for p in params], R, cap)
+        red.bind(grads, compute_stream=comp, side_streams=sides)
+        g0 = [grads[0][v].view(params[v].shape) for v in range(P)]
+        pre = {}
+
+        def hook(v):
+            if sample is None or v in sample:
+                pre[v] = [grads[r][v].cpu().numpy() for r in range(R)]   # before its bucket can launch
+            red.mark_ready(v)
+
+        _mlp_backward(params, g0, X, H, W1, W2, dY0, hook)
+        red.finalize()
+        torch.cuda.synchronize()
+    assert [b for b, _ in red.launch_log()] == list(range(red.num_buckets))
+    for v in range(P):
+        for r in range(1, R):
+            assert torch.equal(grads[r][v], grads[0][v]), (v, r)
+    for v, bufs in pre.items():
+        want = OR.fixed_order_mean(bufs)
+        assert_bits_equal(grads[5][v].cpu().numpy(), want, f"v={v}")
