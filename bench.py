@@ -206,18 +206,24 @@ def run_sync_bench(args, torch, D, WG, WC):
 
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     per_step = []                       # (starts, durations) of every launch, per step
+    ring = 64                           # iterations whose launch events the library keeps
+    read = 0                            # timed steps whose launch times were collected
     torch.cuda.synchronize()            # barrier (one process) + device sync
     t0 = time.perf_counter()
     ev0.record(compute)
     for k in range(args.steps):
         red.sync(order)
-        if flags and k >= 1:
-            per_step.append(red.launch_times_ms(1, True))   # step k-1; step k keeps the GPU busy
+        # Collect launch times of steps that are about to leave the library's
+        # ring, well behind the device, so the host never waits on recent work.
+        while flags and k - read >= ring - 8:
+            per_step.append(red.launch_times_ms(k - read, True))
+            read += 1
     ev1.record(compute)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    if flags:
-        per_step.append(red.launch_times_ms(0, True))
+    while flags and read < args.steps:
+        per_step.append(red.launch_times_ms(args.steps - 1 - read, True))
+        read += 1
     launch_ms = [d for _, ds in per_step for d in ds]
     busy_ms = sum(union_length(st, ds) for st, ds in per_step)
     wall_ms = (t1 - t0) * 1e3 / args.steps

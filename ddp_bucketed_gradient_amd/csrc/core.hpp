@@ -27,7 +27,7 @@ constexpr int64_t kSegElems = 8192;
 constexpr int64_t kFlatAlignElems = 64;
 constexpr int kMaxReplicas = 64;
 // Launch-timing events are kept for this many most recent iterations.
-constexpr int kTimeRing = 4;
+constexpr int kTimeRing = 64;
 
 enum Status : int {
   kOk = 0, kErrArg = -1, kErrIndex = -2, kErrDoubleReady = -3,

@@ -213,7 +213,7 @@ int ddpb_get_launch_log(ddpb_t h, int32_t* buckets, int32_t* trigger_call,
                         int64_t* dev_t0, int64_t* dev_t1, int32_t cap, int32_t* n);
 
 /* With DDPB_BIND_TIME_LAUNCHES: per launched bucket, in launch order, for the
- * finalized iteration `iterations_ago` back (0 = the last one; the last 4
+ * finalized iteration `iterations_ago` back (0 = the last one; the last 64
  * iterations are kept, else DDPB_E_INDEX):
  *   ms[i]        duration from the start of the bucket's first kernel to the
  *                end of its last kernel (hipEvents attached to the dispatches)
