@@ -75,8 +75,15 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
 
 
 class Reducer:
+    """``gradient_as_bucket_view=True`` follows [TP] "Internal Design"
+    (backward pass) and [C30] section "gradient_as_bucket_view": each
+    parameter's gradient *is* its narrowed view of the flat bucket, so the
+    hook copies nothing and the averaged bucket is the averaged gradient. The
+    views are handed out by :meth:`views` and the caller writes gradients
+    into them."""
+
     def __init__(self, numels: Sequence[int], R: int, bucket_cap_bytes: int,
-                 elem_size: int = 4):
+                 elem_size: int = 4, gradient_as_bucket_view: bool = False):
         if R < 1:
             raise ValueError("R must be >= 1")
         self.numels = [int(n) for n in numels]
@@ -93,7 +100,17 @@ class Reducer:
         self.flat = [[np.zeros(n, dtype=np.float32) for n in self.bucket_elems] for _ in range(R)]
         self.averaged = [np.zeros(n, dtype=np.float32) for n in self.bucket_elems]
         self.launch_log: List[Tuple[int, int]] = []   # (bucket, index of triggering mark_ready call)
+        self.as_view = bool(gradient_as_bucket_view)
+        if self.as_view:
+            self.grads = [[self.flat[r][L.bucket][L.offset:L.offset + L.length] for L in self.loc]
+                          for r in range(R)]
         self._reset_iteration()
+
+    def views(self) -> List[List[np.ndarray]]:
+        """R x P gradient views into the flat buckets (bucket-view mode only)."""
+        if not self.as_view:
+            raise RuntimeError("views exist only with gradient_as_bucket_view=True")
+        return self.grads
 
     # -- state ---------------------------------------------------------------
     def _reset_iteration(self):
@@ -103,6 +120,8 @@ class Reducer:
         self.calls = 0
 
     def bind(self, grads: List[List[np.ndarray]]):
+        if self.as_view:
+            raise RuntimeError("in bucket-view mode the gradients are the views; use views()")
         if len(grads) != self.R or any(len(row) != self.P for row in grads):
             raise ValueError("grads must be R x P")
         for row in grads:
@@ -136,8 +155,9 @@ class Reducer:
         call = self.calls
         self.calls += 1
         L = self.loc[v]
-        for r in range(self.R):          # the view copy: bucket.narrow(offset, numel) <- grad
-            self.flat[r][L.bucket][L.offset:L.offset + L.length] = self.grads[r][v]
+        if not self.as_view:             # the view copy: bucket.narrow(offset, numel) <- grad
+            for r in range(self.R):
+                self.flat[r][L.bucket][L.offset:L.offset + L.length] = self.grads[r][v]
         self.pending[L.bucket] -= 1
         if self.pending[L.bucket] == 0:
             self._mark_bucket_ready(L.bucket, call)
@@ -152,10 +172,14 @@ class Reducer:
     def _launch(self, b: int, call: int):
         m = fixed_order_mean([self.flat[r][b] for r in range(self.R)])
         self.averaged[b] = m
-        for v in self.buckets[b]:
-            L = self.loc[v]
+        if self.as_view:                 # the bucket is the gradient storage
             for r in range(self.R):
-                self.grads[r][v][...] = m[L.offset:L.offset + L.length]
+                self.flat[r][b][...] = m
+        else:
+            for v in self.buckets[b]:
+                L = self.loc[v]
+                for r in range(self.R):
+                    self.grads[r][v][...] = m[L.offset:L.offset + L.length]
         self.launch_log.append((b, call))
 
     def finalize(self):
