@@ -45,7 +45,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=3, choices=[2, 3, 4, 5])
     ap.add_argument("--cap-mib", type=float, default=None)
-    ap.add_argument("--mode", choices=["fused", "staged"], default="fused")
+    ap.add_argument("--mode", choices=["fused", "staged", "view"], default="fused",
+                    help="view = gradient_as_bucket_view (gradients live in flat bucket storages)")
     ap.add_argument("--n-side", type=int, default=2,
                     help="side streams; buckets go round-robin over them")
     ap.add_argument("--launch-blocks", type=int, default=None,
@@ -162,13 +163,6 @@ def run_sync_bench(args, torch, D, WG, WC):
     mode = D.MODE_STAGED if args.mode == "staged" else D.MODE_FUSED
     log(f"workload {w.name}: P={P} R={R} S={S / 1e6:.1f} MB cap={w.cap_bytes} mode={args.mode}")
 
-    grads = [[torch.empty(n, dtype=torch.float32, device="cuda") for n in numels] for _ in range(R)]
-    for r in range(R):
-        for v, n in enumerate(numels):
-            WG.normal(WG.seed_of(w.cfg, r, v), n, "cuda", out=grads[r][v])
-    torch.cuda.synchronize()
-    log("inputs generated on the device")
-
     red = D.Reducer([p.shape for p in params], R, w.cap_bytes)
     B = red.num_buckets
     flags = 0 if args.no_time_launches else D.BIND_TIME_LAUNCHES
@@ -178,7 +172,18 @@ def run_sync_bench(args, torch, D, WG, WC):
     compute = torch.cuda.Stream()
     sides = [torch.cuda.Stream() for _ in range(args.n_side)]
     torch.cuda.set_stream(compute)
-    red.bind(grads, compute_stream=compute, side_streams=sides, mode=mode, flags=flags)
+    if args.mode == "view":        # gradient_as_bucket_view: gradients are views of flat storages
+        views = red.bind_bucket_views(compute_stream=compute, side_streams=sides, flags=flags)
+        grads = [[x.view(-1) for x in row] for row in views]
+    else:
+        grads = [[torch.empty(n, dtype=torch.float32, device="cuda") for n in numels] for _ in range(R)]
+    for r in range(R):
+        for v, n in enumerate(numels):
+            WG.normal(WG.seed_of(w.cfg, r, v), n, "cuda", out=grads[r][v])
+    torch.cuda.synchronize()
+    log("inputs generated on the device")
+    if args.mode != "view":
+        red.bind(grads, compute_stream=compute, side_streams=sides, mode=mode, flags=flags)
     red.set_launch_blocks(args.launch_blocks or 0)
     order = w.ready_order()
 
@@ -232,7 +237,8 @@ def run_sync_bench(args, torch, D, WG, WC):
 
     alg = 2 * R * S
     value = alg / (wall_ms * 1e-3) / 1e9
-    kernel = "fused_mean_kernel" if mode == D.MODE_FUSED else "pack+mean+copyback"
+    kernel = {"fused": "fused_mean_kernel", "view": "fused_mean_kernel(bucket view)",
+              "staged": "pack+mean+copyback"}[args.mode]
     roofline = None
     if launch_ms:
         n_launch = len(launch_ms)

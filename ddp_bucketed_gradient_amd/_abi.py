@@ -29,6 +29,7 @@ SYMBOLS = [
     "ddpb_bind", "ddpb_ensure_prior_reduction_finished", "ddpb_mark_ready", "ddpb_mark_ready_many",
     "ddpb_finalize", "ddpb_set_sync", "ddpb_no_sync_accumulate", "ddpb_reset", "ddpb_get_launch_log",
     "ddpb_get_launch_times", "ddpb_device_clock_hz", "ddpb_last_error", "ddpb_set_launch_blocks",
+    "ddpb_view_storage_elems", "ddpb_get_view_offset", "ddpb_bind_bucket_views",
 ]
 
 
@@ -65,6 +66,9 @@ def _sig(lib):
         "ddpb_get_launch_times": [vp, i32, C.POINTER(C.c_float), C.POINTER(C.c_float), i32, P32],
         "ddpb_device_clock_hz": [vp, P64],
         "ddpb_set_launch_blocks": [vp, i32],
+        "ddpb_view_storage_elems": [vp, P64],
+        "ddpb_get_view_offset": [vp, i32, P64],
+        "ddpb_bind_bucket_views": [vp, C.POINTER(vp), i64, vp, C.POINTER(vp), i32, i32],
         "ddpb_last_error": [],
     }
     for name, args in S.items():
@@ -203,6 +207,24 @@ class Lib:
         if with_starts:
             return list(st[:n.value]), list(arr[:n.value])
         return list(arr[:n.value])
+
+    def view_storage_elems(self, h) -> int:
+        n = i64()
+        self._check(self.dll.ddpb_view_storage_elems(h, C.byref(n)))
+        return n.value
+
+    def get_view_offset(self, h, v: int) -> int:
+        n = i64()
+        self._check(self.dll.ddpb_get_view_offset(h, v, C.byref(n)))
+        return n.value
+
+    def bind_bucket_views(self, h, storages: Sequence[int], storage_elems: int, compute_stream: int,
+                          side_streams: Sequence[int], flags: int = 0):
+        st = (vp * max(len(storages), 1))(*[vp(int(p)) for p in storages])
+        ss = (vp * len(side_streams))(*[vp(int(s)) for s in side_streams])
+        self._check(self.dll.ddpb_bind_bucket_views(h, st, int(storage_elems),
+                                                    vp(int(compute_stream)) if compute_stream else None, ss,
+                                                    len(side_streams), flags))
 
     def set_launch_blocks(self, h, max_blocks: int):
         self._check(self.dll.ddpb_set_launch_blocks(h, int(max_blocks)))

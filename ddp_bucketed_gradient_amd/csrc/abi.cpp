@@ -158,6 +158,42 @@ int ddpb_bind(ddpb_t h, void* const* grad_ptrs, void* workspace, int64_t ws_byte
   return pass(h->red.bind(a, &err), err);
 }
 
+int ddpb_view_storage_elems(ddpb_t h, int64_t* elems) {
+  if (!h || !elems) return fail(DDPB_E_ARG, "view_storage_elems: NULL argument");
+  *elems = h->red.plan().flat_elems;
+  return DDPB_OK;
+}
+
+int ddpb_get_view_offset(ddpb_t h, int32_t v, int64_t* offset) {
+  if (!h || !offset) return fail(DDPB_E_ARG, "get_view_offset: NULL argument");
+  const ddpb::Plan& p = h->red.plan();
+  if (v < 0 || v >= p.P) return fail(DDPB_E_INDEX, "get_view_offset: variable index out of range");
+  *offset = p.view_offset(v);
+  return DDPB_OK;
+}
+
+int ddpb_bind_bucket_views(ddpb_t h, void* const* replica_storage, int64_t storage_elems, void* compute_stream,
+                           void* const* side_streams, int32_t n_side, int32_t flags) {
+  if (!h) return fail(DDPB_E_ARG, "bind_bucket_views: NULL handle");
+  const ddpb::Plan& p = h->red.plan();
+  if (flags & ~(DDPB_BIND_DEVICE_TIMESTAMPS | DDPB_BIND_TIME_LAUNCHES))
+    return fail(DDPB_E_ARG, "bind_bucket_views: bad flags");
+  if (n_side < 1 || n_side > 16 || side_streams == nullptr)
+    return fail(DDPB_E_ARG, "bind_bucket_views: need 1..16 side streams");
+  if (storage_elems < p.flat_elems) return fail(DDPB_E_ARG, "bind_bucket_views: storage smaller than needed");
+  if (replica_storage == nullptr) return fail(DDPB_E_ARG, "bind_bucket_views: replica_storage is NULL");
+  ddpb::BindArgs a;
+  a.view_bases.assign(replica_storage, replica_storage + p.R);
+  for (void* s : a.view_bases)
+    if (s == nullptr && p.flat_elems > 0) return fail(DDPB_E_ARG, "bind_bucket_views: NULL storage");
+  a.compute_stream = compute_stream;
+  a.side_streams.assign(side_streams, side_streams + n_side);
+  a.mode = ddpb::kModeBucketView;
+  a.flags = flags;
+  std::string err;
+  return pass(h->red.bind(a, &err), err);
+}
+
 int ddpb_ensure_prior_reduction_finished(ddpb_t h) {
   if (!h) return fail(DDPB_E_ARG, "NULL handle");
   std::string err;

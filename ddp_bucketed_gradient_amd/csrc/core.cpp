@@ -72,6 +72,23 @@ Plan make_plan(const std::vector<int64_t>& numel, int64_t elem_size, int64_t cap
     }
   }
   p.seg_first[B] = static_cast<int32_t>(p.segs.size());
+
+  // Bucket-view work table: the bucket's flat range in kSegElems chunks. Bases
+  // are 64-element aligned, so every chunk starts on a 16-byte boundary.
+  p.view_seg_first.assign(B + 1, 0);
+  for (int32_t b = 0; b < B; ++b) {
+    p.view_seg_first[b] = static_cast<int32_t>(p.view_segs.size());
+    for (int64_t k = 0; k < p.bucket_elems[b]; k += kSegElems) {
+      Segment g;
+      g.var = 0;
+      g.start = p.flat_base[b] + k;
+      g.len = std::min(kSegElems, p.bucket_elems[b] - k);
+      g.boff = k;
+      g.flags = kSegVecBoth;
+      p.view_segs.push_back(g);
+    }
+  }
+  p.view_seg_first[B] = static_cast<int32_t>(p.view_segs.size());
   return p;
 }
 
@@ -98,7 +115,20 @@ int Reducer::bind(const BindArgs& args, std::string* err) {
     *err = "bind: an iteration is in progress";
     return kErrState;
   }
-  const int rc = launcher_->bind(plan_, args, err);
+  int rc;
+  if (args.mode == kModeBucketView) {
+    // The gradient of variable v on replica r is the view at view_offset(v)
+    // of replica r's storage; accumulation addresses it through that pointer.
+    BindArgs a = args;
+    a.grad_ptrs.resize(static_cast<size_t>(plan_.R) * plan_.P);
+    for (int32_t r = 0; r < plan_.R; ++r)
+      for (int32_t v = 0; v < plan_.P; ++v)
+        a.grad_ptrs[static_cast<size_t>(r) * plan_.P + v] =
+            static_cast<char*>(args.view_bases[r]) + plan_.view_offset(v) * plan_.elem_size;
+    rc = launcher_->bind(plan_, a, err);
+  } else {
+    rc = launcher_->bind(plan_, args, err);
+  }
   bound_ = (rc == kOk);
   return rc;
 }

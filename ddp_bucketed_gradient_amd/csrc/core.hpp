@@ -68,6 +68,14 @@ struct Plan {
   std::vector<Segment> segs;                   // bucket by bucket
   std::vector<int32_t> seg_first;              // per bucket, size B + 1
   std::vector<int32_t> seg_bucket;             // per segment
+  // gradient_as_bucket_view: each replica's gradients live in one flat storage
+  // of flat_elems floats in bucket layout; variable v is the view at
+  // flat_base[bucket] + offset. The reduction then walks each bucket's flat
+  // range in kSegElems chunks (var 0 = the replica's storage).
+  std::vector<Segment> view_segs;
+  std::vector<int32_t> view_seg_first;         // per bucket, size B + 1
+
+  int64_t view_offset(int32_t v) const { return flat_base[loc[v].bucket] + loc[v].offset; }
 
   int32_t B() const { return static_cast<int32_t>(members.size()); }
 };
@@ -76,8 +84,11 @@ struct Plan {
 // [C30] "bucket_cap_mb 不是张量切分器"), then locators, flat bases and segments.
 Plan make_plan(const std::vector<int64_t>& numel, int64_t elem_size, int64_t cap_bytes, int32_t R);
 
+enum Mode : int32_t { kModeFused = 0, kModeStaged = 1, kModeBucketView = 2 };
+
 struct BindArgs {
   std::vector<void*> grad_ptrs;     // R * P, replica-major
+  std::vector<void*> view_bases;    // R flat storages (kModeBucketView only)
   void* workspace = nullptr;
   int64_t ws_bytes = 0;
   void* compute_stream = nullptr;

@@ -152,9 +152,12 @@ __global__ __launch_bounds__(kBlock) void fused_mean_kernel(const Segment* __res
     float* p[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) p[r] = grads[static_cast<int64_t>(r) * P + g.var] + g.start;
+    uintptr_t any = 0;                       // 16-byte alignment of every replica's pointer
+#pragma unroll
+    for (int r = 0; r < R; ++r) any |= reinterpret_cast<uintptr_t>(p[r]);
     const int lane = lane_id();
     int tail = 0;
-    if (vec_ok && (g.flags & kSegVecStart)) {
+    if (vec_ok && (g.flags & kSegVecStart) && (any & 15) == 0) {
       const int n4 = len >> 2;
       int i = lane;
       for (; i + 64 * (U - 1) < n4; i += 64 * U) {
@@ -240,7 +243,7 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(const Segment* __restrict_
       const float* src = grads[static_cast<int64_t>(r) * P + g.var] + g.start;
       float* dst = flat + r * flat_stride + fbase + g.boff;
       int tail = 0;
-      if (vec) {
+      if (vec && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
         const int n4 = len >> 2;
         for (int i = lane; i < n4; i += 64) st4(dst + 4 * i, ld4(src + 4 * i));
         tail = n4 * 4;
@@ -305,7 +308,9 @@ __global__ __launch_bounds__(kBlock) void copyback_kernel(const Segment* __restr
     const int len = static_cast<int>(g.len);
     const int lane = lane_id();
     const float* src = avg + fbase + g.boff;
-    const bool vec = vec_ok && (g.flags & kSegVecBoth) == kSegVecBoth;
+    uintptr_t any = 0;
+    for (int r = 0; r < R; ++r) any |= reinterpret_cast<uintptr_t>(grads[static_cast<int64_t>(r) * P + g.var] + g.start);
+    const bool vec = vec_ok && (g.flags & kSegVecBoth) == kSegVecBoth && (any & 15) == 0;
     int tail = 0;
     if (vec) {
       const int n4 = len >> 2;
@@ -348,7 +353,8 @@ __global__ __launch_bounds__(kBlock) void accumulate_kernel(const Segment* __res
   int tail = 0;
   if (BF16) {
     const uint16_t* st = static_cast<const uint16_t*>(steps[k]) + g.start;
-    if (vec_ok && (g.flags & kSegVecStart)) {
+    if (vec_ok && (g.flags & kSegVecStart) && (reinterpret_cast<uintptr_t>(acc) & 15) == 0 &&
+        (reinterpret_cast<uintptr_t>(st) & 7) == 0) {
       const int n4 = len >> 2;
       int i = lane;
       for (; i + 64 * (U - 1) < n4; i += 64 * U) {
@@ -400,7 +406,8 @@ __global__ __launch_bounds__(kBlock) void accumulate_kernel(const Segment* __res
     }
   } else {
     const float* st = static_cast<const float*>(steps[k]) + g.start;
-    if (vec_ok && (g.flags & kSegVecStart)) {
+    if (vec_ok && (g.flags & kSegVecStart) &&
+        ((reinterpret_cast<uintptr_t>(acc) | reinterpret_cast<uintptr_t>(st)) & 15) == 0) {
       const int n4 = len >> 2;
       for (int i = lane; i < n4; i += 64) {
         v4f s4 = ld4(st + 4 * i);
@@ -441,9 +448,7 @@ class HipLauncher final : public Launcher {
     side_used_.assign(side_.size(), 0);
     pow2_ = (R_ & (R_ - 1)) == 0;
     scale_ = 1.0f / static_cast<float>(R_);
-    vec_ok_ = 1;
-    for (void* p : a.grad_ptrs)
-      if (p != nullptr && !aligned(p, 16)) vec_ok_ = 0;
+    vec_ok_ = 1;                // 128-bit paths are chosen per segment from pointer alignment
     flat_ = nullptr;
     avg_ = nullptr;
     if (mode_ == 1) {
@@ -472,6 +477,22 @@ class HipLauncher final : public Launcher {
                             compute_),
              "upload segment table");
     HIP_OK(hipMemsetAsync(d_stamps_, 0, std::max<size_t>(B, 1) * 4 * sizeof(int64_t), compute_), "clear stamps");
+    if (mode_ == kModeBucketView) {
+      for (void* p : a.view_bases)
+        if (!aligned(p, 256)) {
+          *err = "bind_bucket_views: every replica storage must be 256-byte aligned";
+          return kErrArg;
+        }
+      HIP_OK(hipMalloc(&d_view_bases_, std::max<size_t>(R_, 1) * sizeof(float*)), "hipMalloc(view bases)");
+      HIP_OK(hipMalloc(&d_view_segs_, std::max<size_t>(plan.view_segs.size(), 1) * sizeof(Segment)),
+             "hipMalloc(view segments)");
+      HIP_OK(hipMemcpyAsync(d_view_bases_, a.view_bases.data(), R_ * sizeof(float*), hipMemcpyHostToDevice, compute_),
+             "upload view bases");
+      if (!plan.view_segs.empty())
+        HIP_OK(hipMemcpyAsync(d_view_segs_, plan.view_segs.data(), plan.view_segs.size() * sizeof(Segment),
+                              hipMemcpyHostToDevice, compute_),
+               "upload view segments");
+    }
     HIP_OK(hipStreamSynchronize(compute_), "bind: synchronize");
 
     ev_ready_.assign(B, nullptr);
@@ -527,14 +548,12 @@ class HipLauncher final : public Launcher {
   int accumulate(void* const* step_ptrs, int32_t step_dtype, bool first, std::string* err) override {
     const size_t nptr = static_cast<size_t>(R_) * P_;
     if (plan_->segs.empty()) return kOk;
-    int vec = vec_ok_;
-    const uintptr_t need = step_dtype == 1 ? 8 : 16;
+    const int vec = vec_ok_;       // alignment is checked per segment in the kernel
     for (size_t i = 0; i < nptr; ++i) {
       if (step_ptrs[i] == nullptr && plan_->numel[i % P_] > 0) {
         *err = "no_sync_accumulate: NULL step pointer";
         return kErrArg;
       }
-      if (step_ptrs[i] != nullptr && !aligned(step_ptrs[i], need)) vec = 0;
     }
     // Step pointer tables go through a small ring of device slots; a table
     // seen recently is reused without another upload.
@@ -622,24 +641,30 @@ class HipLauncher final : public Launcher {
 
  private:
   int enqueue_bucket(int32_t b, hipStream_t s, hipEvent_t t0, hipEvent_t t1, std::string* err) {
-    const int32_t s0 = plan_->seg_first[b];
-    const int32_t nseg = plan_->seg_first[b + 1] - s0;
+    // Bucket-view mode runs the same fused kernel over the bucket's flat range
+    // of each replica's storage (one pseudo-variable per replica).
+    const bool view = (mode_ == kModeBucketView);
+    const std::vector<int32_t>& first = view ? plan_->view_seg_first : plan_->seg_first;
+    const int32_t s0 = first[b];
+    const int32_t nseg = first[b + 1] - s0;
     if (nseg == 0) {                          // bucket of empty tensors: nothing to move
       if (t0) HIP_OK(hipEventRecord(t0, s), "hipEventRecord(t0)");
       if (t1) HIP_OK(hipEventRecord(t1, s), "hipEventRecord(t1)");
       return kOk;
     }
-    const Segment* segs = d_segs_ + s0;
+    const Segment* segs = (view ? d_view_segs_ : d_segs_) + s0;
+    float* const* table = view ? d_view_bases_ : d_grads_;
+    const int32_t tp = view ? 1 : P_;
     int64_t* stamp = (flags_ & 1) ? d_stamps_ + static_cast<int64_t>(b) * 4 : nullptr;
     int64_t blocks = (nseg + kWavesPerBlock - 1) / kWavesPerBlock;
     if (max_blocks_ > 0) blocks = std::min<int64_t>(blocks, max_blocks_);
     const dim3 grid(static_cast<unsigned>(blocks));
     const dim3 block(kBlock);
-    if (mode_ == 0) {
+    if (mode_ == kModeFused || view) {
       switch (R_) {
 #define DDPB_FUSED_CASE(RR)                                                                                      \
   case RR:                                                                                                       \
-    hipExtLaunchKernelGGL((fused_mean_kernel<RR>), grid, block, 0, s, t0, t1, 0, segs, nseg, d_grads_, P_, scale_, \
+    hipExtLaunchKernelGGL((fused_mean_kernel<RR>), grid, block, 0, s, t0, t1, 0, segs, nseg, table, tp, scale_,   \
                           vec_ok_, stamp);                                                                       \
     break;
         DDPB_FUSED_CASE(1) DDPB_FUSED_CASE(2) DDPB_FUSED_CASE(3) DDPB_FUSED_CASE(4)
@@ -648,7 +673,7 @@ class HipLauncher final : public Launcher {
         DDPB_FUSED_CASE(13) DDPB_FUSED_CASE(14) DDPB_FUSED_CASE(15) DDPB_FUSED_CASE(16)
 #undef DDPB_FUSED_CASE
         default:
-          hipExtLaunchKernelGGL(fused_mean_kernel_rt, grid, block, 0, s, t0, t1, 0, segs, nseg, d_grads_, P_, R_,
+          hipExtLaunchKernelGGL(fused_mean_kernel_rt, grid, block, 0, s, t0, t1, 0, segs, nseg, table, tp, R_,
                                 scale_, pow2_ ? 1 : 0, stamp);
       }
       HIP_OK(hipGetLastError(), "launch fused_mean_kernel");
@@ -701,6 +726,10 @@ class HipLauncher final : public Launcher {
     if (d_segs_) (void)hipFree(d_segs_);
     if (d_stamps_) (void)hipFree(d_stamps_);
     if (d_steps_) (void)hipFree(d_steps_);
+    if (d_view_bases_) (void)hipFree(d_view_bases_);
+    if (d_view_segs_) (void)hipFree(d_view_segs_);
+    d_view_bases_ = nullptr;
+    d_view_segs_ = nullptr;
     if (h_steps_) (void)hipHostFree(h_steps_);
     d_grads_ = nullptr;
     d_segs_ = nullptr;
@@ -723,6 +752,8 @@ class HipLauncher final : public Launcher {
   Segment* d_segs_ = nullptr;
   int64_t* d_stamps_ = nullptr;
   void** d_steps_ = nullptr;
+  float** d_view_bases_ = nullptr;
+  Segment* d_view_segs_ = nullptr;
   void** h_steps_ = nullptr;
   float* flat_ = nullptr;
   float* avg_ = nullptr;

@@ -75,6 +75,36 @@ class Reducer:
         self.lib.bind(self.h, ptrs, ws.data_ptr() if ws is not None else 0, nbytes, compute.cuda_stream,
                       [s.cuda_stream for s in sides], mode, flags)
 
+    def bind_bucket_views(self, device=None, compute_stream=None, side_streams=None, flags: int = 0):
+        """gradient_as_bucket_view: allocate one flat fp32 storage per replica
+        in bucket layout, bind it, and return R x P gradient views into it
+        (shaped like the parameters). Write each replica's gradients into its
+        views; the reduction averages them in place."""
+        import torch
+        dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        n = self.lib.view_storage_elems(self.h)
+        stores = [torch.zeros(max(n, 1), dtype=torch.float32, device=dev) for _ in range(self.R)]
+        views = []
+        for r in range(self.R):
+            row = []
+            for v, shape in enumerate(self.shapes):
+                off = self.lib.get_view_offset(self.h, v)
+                numel = 1
+                for d in shape:
+                    numel *= d
+                row.append(stores[r][off:off + numel].view(shape))
+            views.append(row)
+        compute = compute_stream if compute_stream is not None else torch.cuda.current_stream(dev)
+        sides = list(side_streams) if side_streams else [torch.cuda.Stream(device=dev) for _ in range(2)]
+        self._keep = [stores, views, compute, sides]
+        self.compute_stream, self.side_streams, self.workspace = compute, sides, None
+        self.lib.bind_bucket_views(self.h, [s.data_ptr() for s in stores], n, compute.cuda_stream,
+                                   [s.cuda_stream for s in sides], flags)
+        return views
+
+    def view_offset(self, v: int) -> int:
+        return self.lib.get_view_offset(self.h, v)
+
     def bind_ptrs(self, ptrs: Sequence[int], workspace: int = 0, ws_bytes: int = 0, compute_stream: int = 0,
                   side_streams: Sequence[int] = (0,), mode: int = MODE_FUSED, flags: int = 0):
         """Raw-pointer bind (used by the host-only tests)."""

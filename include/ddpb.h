@@ -138,6 +138,26 @@ int ddpb_bind(ddpb_t h, void* const* grad_ptrs, void* workspace, int64_t ws_byte
               void* compute_stream, void* const* side_streams, int32_t n_side,
               int32_t mode, int32_t flags);
 
+/* gradient_as_bucket_view ([TP] "Internal Design", backward pass; [C30]
+ * section "gradient_as_bucket_view"; [PDTI] §4): each replica keeps all its
+ * gradients in one flat fp32 storage laid out bucket by bucket, and the
+ * gradient of variable v is the view of numel[v] elements at element offset
+ * ddpb_get_view_offset(v) (bucket base, 64-element aligned, plus the
+ * locator's offset). The hook then copies nothing and the bucket's reduction
+ * walks its flat range contiguously.
+ *   ddpb_view_storage_elems   elements each replica's storage must hold
+ *   ddpb_get_view_offset      element offset of variable v in that storage
+ *   ddpb_bind_bucket_views    R device pointers to the storages (replica r's
+ *                             first; 256-byte aligned, >= storage_elems fp32
+ *                             each, caller-owned), streams and flags as in
+ *                             ddpb_bind. ddpb_no_sync_accumulate and every
+ *                             other call work unchanged on the views. */
+int ddpb_view_storage_elems(ddpb_t h, int64_t* elems);
+int ddpb_get_view_offset(ddpb_t h, int32_t v, int64_t* offset);
+int ddpb_bind_bucket_views(ddpb_t h, void* const* replica_storage, int64_t storage_elems,
+                           void* compute_stream, void* const* side_streams, int32_t n_side,
+                           int32_t flags);
+
 /* Caps the number of workgroups (256 threads each) of every reduction launch;
  * 0 (the default) launches one workgroup per four segments, so a bucket uses
  * the whole GPU. A small cap keeps the reduction on a few compute units while
