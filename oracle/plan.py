@@ -24,12 +24,21 @@ from typing import List, Sequence
 
 
 def compute_bucket_assignment_by_size(numels: Sequence[int], elem_size: int,
-                                      cap_bytes: int) -> List[List[int]]:
-    """Return the buckets as lists of variable indices, bucket 0 first."""
+                                      cap_bytes: int, order: Sequence[int] = None) -> List[List[int]]:
+    """Return the buckets as lists of variable indices, bucket 0 first.
+
+    ``order`` is the visiting order: by default the reverse of the definition
+    order; a bucket rebuild passes the order in which the gradients became
+    ready in a finished iteration ([C30] "第一次迭代为何不同": the rebuilt
+    parameters are packed in their actual ready order with the same rule)."""
+    if order is None:
+        order = range(len(numels) - 1, -1, -1)
+    elif sorted(order) != list(range(len(numels))):
+        raise ValueError("order must be a permutation of the variable indices")
     buckets: List[List[int]] = []
     current: List[int] = []
     size = 0
-    for v in range(len(numels) - 1, -1, -1):
+    for v in order:
         current.append(v)
         size += int(numels[v]) * int(elem_size)
         if size >= cap_bytes:

@@ -89,22 +89,46 @@ class Reducer:
         self.numels = [int(n) for n in numels]
         self.P = len(self.numels)
         self.R = R
-        self.buckets = compute_bucket_assignment_by_size(self.numels, elem_size, bucket_cap_bytes)
-        self.loc = locators(self.buckets, self.numels)
-        self.B = len(self.buckets)
-        self.bucket_elems = bucket_numels(self.buckets, self.numels)
+        self.elem_size = elem_size
+        self.cap = bucket_cap_bytes
         self.sync_enabled = True
         self.failed = False
         self.grads: Optional[List[List[np.ndarray]]] = None
-        # per-replica flat buckets (the pages' flat bucket buffers)
-        self.flat = [[np.zeros(n, dtype=np.float32) for n in self.bucket_elems] for _ in range(R)]
-        self.averaged = [np.zeros(n, dtype=np.float32) for n in self.bucket_elems]
         self.launch_log: List[Tuple[int, int]] = []   # (bucket, index of triggering mark_ready call)
         self.as_view = bool(gradient_as_bucket_view)
+        self.order_now: List[int] = []                # hooks of the current iteration, in order
+        self.last_ready_order: Optional[List[int]] = None
+        self._plan(compute_bucket_assignment_by_size(self.numels, elem_size, bucket_cap_bytes))
+        self._reset_iteration()
+
+    def _plan(self, buckets: List[List[int]]):
+        self.buckets = buckets
+        self.loc = locators(self.buckets, self.numels)
+        self.B = len(self.buckets)
+        self.bucket_elems = bucket_numels(self.buckets, self.numels)
+        # per-replica flat buckets (the pages' flat bucket buffers)
+        self.flat = [[np.zeros(n, dtype=np.float32) for n in self.bucket_elems] for _ in range(self.R)]
+        self.averaged = [np.zeros(n, dtype=np.float32) for n in self.bucket_elems]
         if self.as_view:
             self.grads = [[self.flat[r][L.bucket][L.offset:L.offset + L.length] for L in self.loc]
-                          for r in range(R)]
-        self._reset_iteration()
+                          for r in range(self.R)]
+
+    def rebuild_buckets(self, bucket_cap_bytes: Optional[int] = None) -> bool:
+        """Re-plan from the order in which the hooks fired in the last finished
+        iteration ([C30] "第一次迭代为何不同"): the rebuild needs the prior
+        reduction to be complete, then packs the parameters in their ready
+        order with the same cap rule. Returns False when no finished iteration
+        was recorded. In bucket-view mode the views are new (re-fetch them)."""
+        if self.failed or self.calls:
+            raise ReductionIncomplete("rebuild needs the prior iteration to have finished reducing")
+        if self.last_ready_order is None:
+            return False
+        if bucket_cap_bytes is not None:
+            self.cap = bucket_cap_bytes
+        self._plan(compute_bucket_assignment_by_size(self.numels, self.elem_size, self.cap,
+                                                     order=self.last_ready_order))
+        self._reset_iteration()              # copying mode: the caller's gradients stay bound
+        return True
 
     def views(self) -> List[List[np.ndarray]]:
         """R x P gradient views into the flat buckets (bucket-view mode only)."""
@@ -118,6 +142,7 @@ class Reducer:
         self.ready = [False] * self.P
         self.next_bucket = 0
         self.calls = 0
+        self.order_now = []
 
     def bind(self, grads: List[List[np.ndarray]]):
         if self.as_view:
@@ -152,6 +177,7 @@ class Reducer:
         if self.ready[v]:
             raise DoubleReady(v)
         self.ready[v] = True
+        self.order_now.append(v)
         call = self.calls
         self.calls += 1
         L = self.loc[v]
@@ -189,6 +215,7 @@ class Reducer:
             self.failed = True
             raise ReductionIncomplete(
                 f"only {self.next_bucket} of {self.B} buckets were reduced")
+        self.last_ready_order = list(self.order_now)
         self._reset_iteration()
 
     def reset(self):
