@@ -30,6 +30,7 @@ SYMBOLS = [
     "ddpb_finalize", "ddpb_set_sync", "ddpb_no_sync_accumulate", "ddpb_reset", "ddpb_get_launch_log",
     "ddpb_get_launch_times", "ddpb_device_clock_hz", "ddpb_last_error", "ddpb_set_launch_blocks",
     "ddpb_view_storage_elems", "ddpb_get_view_offset", "ddpb_bind_bucket_views",
+    "ddpb_rebuild_buckets", "ddpb_get_ready_order",
 ]
 
 
@@ -66,6 +67,8 @@ def _sig(lib):
         "ddpb_get_launch_times": [vp, i32, C.POINTER(C.c_float), C.POINTER(C.c_float), i32, P32],
         "ddpb_device_clock_hz": [vp, P64],
         "ddpb_set_launch_blocks": [vp, i32],
+        "ddpb_rebuild_buckets": [vp, i64],
+        "ddpb_get_ready_order": [vp, P32, i32, P32],
         "ddpb_view_storage_elems": [vp, P64],
         "ddpb_get_view_offset": [vp, i32, P64],
         "ddpb_bind_bucket_views": [vp, C.POINTER(vp), i64, vp, C.POINTER(vp), i32, i32],
@@ -206,6 +209,16 @@ class Lib:
         self._check(self.dll.ddpb_get_launch_times(h, iterations_ago, st, arr, n.value, C.byref(n)))
         if with_starts:
             return list(st[:n.value]), list(arr[:n.value])
+        return list(arr[:n.value])
+
+    def rebuild_buckets(self, h, bucket_cap_bytes: int):
+        self._check(self.dll.ddpb_rebuild_buckets(h, int(bucket_cap_bytes)))
+
+    def get_ready_order(self, h) -> List[int]:
+        n = i32()
+        self._check(self.dll.ddpb_get_ready_order(h, None, 0, C.byref(n)))
+        arr = (C.c_int32 * max(n.value, 1))()
+        self._check(self.dll.ddpb_get_ready_order(h, arr, n.value, C.byref(n)))
         return list(arr[:n.value])
 
     def view_storage_elems(self, h) -> int:

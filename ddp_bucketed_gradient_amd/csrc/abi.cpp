@@ -158,6 +158,20 @@ int ddpb_bind(ddpb_t h, void* const* grad_ptrs, void* workspace, int64_t ws_byte
   return pass(h->red.bind(a, &err), err);
 }
 
+int ddpb_rebuild_buckets(ddpb_t h, int64_t bucket_cap_bytes) {
+  if (!h) return fail(DDPB_E_ARG, "rebuild_buckets: NULL handle");
+  std::string err;
+  return pass(h->red.rebuild_buckets(bucket_cap_bytes, &err), err);
+}
+
+int ddpb_get_ready_order(ddpb_t h, int32_t* order, int32_t cap, int32_t* n) {
+  if (!h || !n || cap < 0 || (cap > 0 && !order)) return fail(DDPB_E_ARG, "get_ready_order: bad argument");
+  const auto& o = h->red.last_ready_order();
+  *n = static_cast<int32_t>(o.size());
+  for (int32_t i = 0; i < std::min<int32_t>(cap, *n); ++i) order[i] = o[i];
+  return DDPB_OK;
+}
+
 int ddpb_view_storage_elems(ddpb_t h, int64_t* elems) {
   if (!h || !elems) return fail(DDPB_E_ARG, "view_storage_elems: NULL argument");
   *elems = h->red.plan().flat_elems;

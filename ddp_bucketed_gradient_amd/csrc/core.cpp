@@ -9,7 +9,8 @@ namespace ddpb {
 
 static int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
-Plan make_plan(const std::vector<int64_t>& numel, int64_t elem_size, int64_t cap_bytes, int32_t R) {
+Plan make_plan(const std::vector<int64_t>& numel, int64_t elem_size, int64_t cap_bytes, int32_t R,
+               const std::vector<int32_t>* order) {
   Plan p;
   p.P = static_cast<int32_t>(numel.size());
   p.R = R;
@@ -22,7 +23,8 @@ Plan make_plan(const std::vector<int64_t>& numel, int64_t elem_size, int64_t cap
   // size reaches or exceeds the cap; the last, partly filled bucket is kept.
   std::vector<int32_t> cur;
   int64_t size = 0;
-  for (int32_t v = p.P - 1; v >= 0; --v) {
+  for (int32_t i = 0; i < p.P; ++i) {
+    const int32_t v = order ? (*order)[i] : p.P - 1 - i;
     cur.push_back(v);
     size += numel[v] * elem_size;
     if (size >= cap_bytes) {
@@ -108,6 +110,7 @@ void Reducer::begin_iteration() {
   ready_.assign(plan_.P, 0);
   next_bucket_ = 0;
   calls_ = 0;
+  order_now_.clear();
 }
 
 int Reducer::bind(const BindArgs& args, std::string* err) {
@@ -164,6 +167,7 @@ int Reducer::mark_ready(int32_t v, std::string* err) {
   }
   if (calls_ == 0) log_.clear();
   ready_[v] = 1;
+  order_now_.push_back(v);
   const int32_t call = calls_++;
   const int32_t b = plan_.loc[v].bucket;
   // [Li] per-hook logic: decrement the bucket's pending count; at zero the
@@ -201,6 +205,8 @@ int Reducer::finalize(std::string* err) {
   // every bucket's reduction, without a host synchronization.
   const int rc = launcher_->join(err);
   log_ring_[finalized_ % kTimeRing] = log_;
+  last_order_ = order_now_;
+  has_order_ = true;
   ++finalized_;
   begin_iteration();
   return rc;
@@ -225,6 +231,26 @@ int Reducer::accumulate(void* const* step_ptrs, int32_t step_dtype, bool first, 
     return kErrArg;
   }
   return launcher_->accumulate(step_ptrs, step_dtype, first, err);
+}
+
+int Reducer::rebuild_buckets(int64_t cap_bytes, std::string* err) {
+  if (failed_ || iteration_open()) {
+    *err = "rebuild_buckets: the prior iteration has not finished reducing";
+    return kErrIncomplete;
+  }
+  if (!has_order_) {
+    *err = "rebuild_buckets: no finished iteration has recorded a ready order yet";
+    return kErrState;
+  }
+  if (cap_bytes < 0) {
+    *err = "rebuild_buckets: negative bucket cap";
+    return kErrArg;
+  }
+  const std::vector<int32_t> order = last_order_;
+  plan_ = make_plan(plan_.numel, plan_.elem_size, cap_bytes, plan_.R, &order);
+  bound_ = false;                  // device tables and events follow the new plan at the next bind
+  begin_iteration();
+  return kOk;
 }
 
 int Reducer::reset() {

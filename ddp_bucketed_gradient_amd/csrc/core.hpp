@@ -82,7 +82,10 @@ struct Plan {
 
 // Reverse-order greedy assignment under the cap ([Li] "Gradient Bucketing";
 // [C30] "bucket_cap_mb 不是张量切分器"), then locators, flat bases and segments.
-Plan make_plan(const std::vector<int64_t>& numel, int64_t elem_size, int64_t cap_bytes, int32_t R);
+// `order` (optional) is the visiting order; default is the reverse of the
+// definition order, a rebuild passes the learned ready order.
+Plan make_plan(const std::vector<int64_t>& numel, int64_t elem_size, int64_t cap_bytes, int32_t R,
+               const std::vector<int32_t>* order = nullptr);
 
 enum Mode : int32_t { kModeFused = 0, kModeStaged = 1, kModeBucketView = 2 };
 
@@ -146,6 +149,10 @@ class Reducer {
   int set_sync(bool enabled, std::string* err);
   int accumulate(void* const* step_ptrs, int32_t step_dtype, bool first, std::string* err);
   int reset();
+  // [C30] "第一次迭代为何不同": re-plan from the hook order of the last finished
+  // iteration (same cap rule); the handle must be bound again afterwards.
+  int rebuild_buckets(int64_t cap_bytes, std::string* err);
+  const std::vector<int32_t>& last_ready_order() const { return last_order_; }
   const std::vector<LaunchRecord>& log() const { return log_; }
   int64_t finalized() const { return finalized_; }
   // Launches of finalized iteration `it` (only the last kTimeRing are kept).
@@ -166,6 +173,9 @@ class Reducer {
   int32_t next_bucket_ = 0;
   int32_t calls_ = 0;              // mark_ready calls that counted, this iteration
   std::vector<LaunchRecord> log_;
+  std::vector<int32_t> order_now_;   // hook order of the current iteration
+  std::vector<int32_t> last_order_;  // ... of the last finished iteration
+  bool has_order_ = false;
   int64_t finalized_ = 0;          // iterations finalized so far
   std::vector<LaunchRecord> log_ring_[kTimeRing];
 };

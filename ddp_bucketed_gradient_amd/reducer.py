@@ -102,6 +102,17 @@ class Reducer:
                                    [s.cuda_stream for s in sides], flags)
         return views
 
+    def rebuild_buckets(self, bucket_cap_bytes: Optional[int] = None):
+        """Re-plan the buckets from the last finished iteration's hook order.
+        The reducer must be bound again afterwards (``bind`` or
+        ``bind_bucket_views``; views change)."""
+        if bucket_cap_bytes is not None:
+            self.cap = int(bucket_cap_bytes)
+        self.lib.rebuild_buckets(self.h, self.cap)
+
+    def ready_order(self) -> List[int]:
+        return self.lib.get_ready_order(self.h)
+
     def view_offset(self, v: int) -> int:
         return self.lib.get_view_offset(self.h, v)
 

@@ -138,6 +138,22 @@ int ddpb_bind(ddpb_t h, void* const* grad_ptrs, void* workspace, int64_t ws_byte
               void* compute_stream, void* const* side_streams, int32_t n_side,
               int32_t mode, int32_t flags);
 
+/* Ready-order bucket rebuild ([C30] "第一次迭代为何不同"): re-plans the buckets
+ * from the order in which the hooks fired in the last finished iteration,
+ * first-ready variable first, with the same rule (whole tensors, the bucket
+ * closes once its size is >= bucket_cap_bytes), so buckets follow the real
+ * backward order and no bucket waits on a later gradient. A first iteration
+ * planned with a huge cap (one bucket) learns the order without reducing
+ * early. Needs a finished iteration and none in progress (DDPB_E_STATE /
+ * DDPB_E_INCOMPLETE otherwise). Afterwards the plan queries describe the new
+ * buckets and the handle must be bound again (ddpb_bind or
+ * ddpb_bind_bucket_views; view offsets change). */
+int ddpb_rebuild_buckets(ddpb_t h, int64_t bucket_cap_bytes);
+
+/* Hook order of the last finished iteration (variable indices, first hook
+ * first). Writes min(cap, count) entries and sets *n = count. */
+int ddpb_get_ready_order(ddpb_t h, int32_t* order, int32_t cap, int32_t* n);
+
 /* gradient_as_bucket_view ([TP] "Internal Design", backward pass; [C30]
  * section "gradient_as_bucket_view"; [PDTI] §4): each replica keeps all its
  * gradients in one flat fp32 storage laid out bucket by bucket, and the

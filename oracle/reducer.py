@@ -98,6 +98,7 @@ class Reducer:
         self.as_view = bool(gradient_as_bucket_view)
         self.order_now: List[int] = []                # hooks of the current iteration, in order
         self.last_ready_order: Optional[List[int]] = None
+        self.used_acc: Optional[np.ndarray] = None    # R x P used flags, OR-ed over no_sync steps
         self._plan(compute_bucket_assignment_by_size(self.numels, elem_size, bucket_cap_bytes))
         self._reset_iteration()
 
@@ -167,6 +168,48 @@ class Reducer:
                 "prior iteration did not finish reducing every bucket")
 
     # -- hooks ---------------------------------------------------------------
+    # -- unused parameters ---------------------------------------------------
+    def set_local_used(self, used):
+        """Which replicas used which variables in the coming backward pass
+        (R x P booleans), as the forward's graph walk would find them ([Li]
+        "Handling Unused Parameters"; [TP] forward pass with
+        find_unused_parameters). Under no_sync the flags of successive calls
+        are OR-ed together and serve the next synchronisation ([Li] "Gradient
+        Accumulation (no_sync)"). Without any call every variable is used."""
+        if self.calls:
+            raise RuntimeError("set_local_used must come before the iteration's hooks")
+        u = np.asarray(used, dtype=bool).reshape(self.R, self.P)
+        self.used_acc = u.copy() if self.used_acc is None else (self.used_acc | u)
+
+    def globally_used(self) -> np.ndarray:
+        """The OR over replicas of the used flags (the bitmap all-reduce)."""
+        if self.used_acc is None:
+            return np.ones(self.P, dtype=bool)
+        return self.used_acc.any(axis=0)
+
+    def _zero_slices(self, r: int, v: int):
+        L = self.loc[v]
+        self.flat[r][L.bucket][L.offset:L.offset + L.length] = 0.0
+
+    def _mark_unused_ready(self, call: int):
+        """At the iteration's first hook: zero the bucket slices of variables a
+        replica did not use, and treat globally unused variables as ready."""
+        if self.used_acc is None:
+            return
+        G = self.globally_used()
+        for r in range(self.R):
+            for v in range(self.P):
+                if not self.used_acc[r, v]:
+                    self._zero_slices(r, v)
+        for v in range(self.P):
+            if not G[v]:
+                self.ready[v] = True
+                b = self.loc[v].bucket
+                self.pending[b] -= 1
+                if self.pending[b] == 0:
+                    self._mark_bucket_ready(b, call)
+
+    # -- hooks ---------------------------------------------------------------
     def mark_ready(self, v: int):
         if not (0 <= v < self.P):
             raise IndexError(v)
@@ -174,16 +217,21 @@ class Reducer:
             return
         if self.failed:
             raise ReductionIncomplete("prior iteration did not finish reducing every bucket")
+        call = self.calls
+        if call == 0:
+            self._mark_unused_ready(call)
         if self.ready[v]:
             raise DoubleReady(v)
         self.ready[v] = True
         self.order_now.append(v)
-        call = self.calls
         self.calls += 1
         L = self.loc[v]
         if not self.as_view:             # the view copy: bucket.narrow(offset, numel) <- grad
             for r in range(self.R):
-                self.flat[r][L.bucket][L.offset:L.offset + L.length] = self.grads[r][v]
+                if self.used_acc is not None and not self.used_acc[r, v]:
+                    self._zero_slices(r, v)  # a replica without this gradient contributes zeros
+                else:
+                    self.flat[r][L.bucket][L.offset:L.offset + L.length] = self.grads[r][v]
         self.pending[L.bucket] -= 1
         if self.pending[L.bucket] == 0:
             self._mark_bucket_ready(L.bucket, call)
@@ -202,7 +250,10 @@ class Reducer:
             for r in range(self.R):
                 self.flat[r][b][...] = m
         else:
+            G = self.globally_used()
             for v in self.buckets[b]:
+                if not G[v]:
+                    continue             # globally unused: its gradients are left untouched
                 L = self.loc[v]
                 for r in range(self.R):
                     self.grads[r][v][...] = m[L.offset:L.offset + L.length]
@@ -211,11 +262,16 @@ class Reducer:
     def finalize(self):
         if not self.sync_enabled and self.calls == 0:
             return
+        if self.calls == 0:
+            self._mark_unused_ready(0)   # no hook fired: only unused variables, if any
         if self.next_bucket != self.B:
             self.failed = True
             raise ReductionIncomplete(
                 f"only {self.next_bucket} of {self.B} buckets were reduced")
-        self.last_ready_order = list(self.order_now)
+        # a rebuild needs every variable's place in the ready order; an
+        # iteration with unused variables does not give one
+        self.last_ready_order = list(self.order_now) if len(self.order_now) == self.P else None
+        self.used_acc = None             # the flags served this synchronisation
         self._reset_iteration()
 
     def reset(self):
@@ -226,10 +282,16 @@ class Reducer:
     def no_sync_accumulate(self, step: List[List[np.ndarray]], first: bool):
         """One local backward's contribution: ``grad = step`` on the first
         micro-step, ``grad += step`` afterwards (float32). ``step`` holds
-        float32 arrays, or uint16 arrays of bf16 bit patterns."""
+        float32 arrays, or uint16 arrays of bf16 bit patterns; ``None`` means
+        that replica produced no gradient for that variable (it contributes
+        zeros)."""
         for r in range(self.R):
             for v in range(self.P):
                 s = step[r][v]
+                if s is None:
+                    if first:
+                        self.grads[r][v][...] = 0.0
+                    continue
                 s32 = bf16_bits_to_f32(s) if s.dtype == np.uint16 else np.asarray(s, dtype=np.float32)
                 if first:
                     self.grads[r][v][...] = s32
