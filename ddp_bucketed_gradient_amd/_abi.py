@@ -30,7 +30,7 @@ SYMBOLS = [
     "ddpb_finalize", "ddpb_set_sync", "ddpb_no_sync_accumulate", "ddpb_reset", "ddpb_get_launch_log",
     "ddpb_get_launch_times", "ddpb_device_clock_hz", "ddpb_last_error", "ddpb_set_launch_blocks",
     "ddpb_view_storage_elems", "ddpb_get_view_offset", "ddpb_bind_bucket_views",
-    "ddpb_rebuild_buckets", "ddpb_get_ready_order",
+    "ddpb_rebuild_buckets", "ddpb_get_ready_order", "ddpb_set_local_used",
 ]
 
 
@@ -67,6 +67,7 @@ def _sig(lib):
         "ddpb_get_launch_times": [vp, i32, C.POINTER(C.c_float), C.POINTER(C.c_float), i32, P32],
         "ddpb_device_clock_hz": [vp, P64],
         "ddpb_set_launch_blocks": [vp, i32],
+        "ddpb_set_local_used": [vp, C.POINTER(C.c_uint8)],
         "ddpb_rebuild_buckets": [vp, i64],
         "ddpb_get_ready_order": [vp, P32, i32, P32],
         "ddpb_view_storage_elems": [vp, P64],
@@ -179,7 +180,7 @@ class Lib:
         self._check(self.dll.ddpb_set_sync(h, 1 if enabled else 0))
 
     def no_sync_accumulate(self, h, step_ptrs: Sequence[int], step_dtype: int, first_step: bool):
-        sp = (vp * max(len(step_ptrs), 1))(*[vp(int(p)) for p in step_ptrs])
+        sp = (vp * max(len(step_ptrs), 1))(*[vp(int(p)) if p else vp() for p in step_ptrs])
         self._check(self.dll.ddpb_no_sync_accumulate(h, sp, step_dtype, 1 if first_step else 0))
 
     def reset(self, h):
@@ -241,6 +242,14 @@ class Lib:
 
     def set_launch_blocks(self, h, max_blocks: int):
         self._check(self.dll.ddpb_set_launch_blocks(h, int(max_blocks)))
+
+    def set_local_used(self, h, used: Optional[Sequence[int]]):
+        """used: R*P flags, replica-major, or None for all used."""
+        if used is None:
+            self._check(self.dll.ddpb_set_local_used(h, None))
+            return
+        buf = (C.c_uint8 * max(len(used), 1))(*[1 if u else 0 for u in used])
+        self._check(self.dll.ddpb_set_local_used(h, buf))
 
     def device_clock_hz(self, h) -> int:
         hz = i64()

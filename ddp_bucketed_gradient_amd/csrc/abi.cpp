@@ -302,6 +302,12 @@ int ddpb_get_launch_times(ddpb_t h, int32_t iterations_ago, float* start_ms, flo
   return DDPB_OK;
 }
 
+int ddpb_set_local_used(ddpb_t h, const uint8_t* used) {
+  if (!h) return fail(DDPB_E_ARG, "NULL handle");
+  std::string err;
+  return pass(h->red.set_local_used(used, &err), err);
+}
+
 int ddpb_set_launch_blocks(ddpb_t h, int32_t max_blocks) {
   if (!h || max_blocks < 0) return fail(DDPB_E_ARG, "set_launch_blocks: bad argument");
   h->red.launcher()->set_max_blocks(max_blocks);

@@ -161,11 +161,15 @@ int Reducer::mark_ready(int32_t v, std::string* err) {
     *err = "Expected to have finished reduction in the prior iteration before starting a new one";
     return kErrIncomplete;
   }
+  if (calls_ == 0) {
+    log_.clear();
+    const int rc = mark_unused_ready(0, err);   // before the iteration's first hook
+    if (rc != kOk) return rc;
+  }
   if (ready_[v]) {
     *err = "mark_ready: variable marked ready twice in one iteration";
     return kErrDoubleReady;
   }
-  if (calls_ == 0) log_.clear();
   ready_[v] = 1;
   order_now_.push_back(v);
   const int32_t call = calls_++;
@@ -174,18 +178,53 @@ int Reducer::mark_ready(int32_t v, std::string* err) {
   // bucket is ready. [C30] "Bucket 必须按序发起": only the bucket at
   // next_bucket_ may launch, followed by every already complete successor; a
   // later bucket that completes first stays parked.
-  if (--pending_[b] == 0 && b == next_bucket_) {
-    const int32_t first = next_bucket_;
-    while (next_bucket_ < plan_.B() && pending_[next_bucket_] == 0) {
-      log_.push_back(LaunchRecord{next_bucket_, call});
-      ++next_bucket_;
-    }
-    const int rc = launcher_->launch(first, next_bucket_ - 1, finalized_, err);
-    if (rc != kOk) {
-      failed_ = true;
-      return rc;
-    }
+  if (--pending_[b] == 0 && b == next_bucket_) return launch_ready(call, err);
+  return kOk;
+}
+
+int Reducer::launch_ready(int32_t call, std::string* err) {
+  const int32_t first = next_bucket_;
+  while (next_bucket_ < plan_.B() && pending_[next_bucket_] == 0) {
+    log_.push_back(LaunchRecord{next_bucket_, call});
+    ++next_bucket_;
   }
+  if (next_bucket_ == first) return kOk;
+  const int rc = launcher_->launch(first, next_bucket_ - 1, finalized_, err);
+  if (rc != kOk) failed_ = true;
+  return rc;
+}
+
+// [Li] "Handling Unused Parameters": variables no replica used are treated as
+// ready (their buckets can complete) and their gradients are left alone; a
+// replica that did not use a variable contributes zeros. [C30] "Unused
+// Parameter": this happens when the iteration's first hook fires.
+int Reducer::mark_unused_ready(int32_t call, std::string* err) {
+  if (!used_set_) return kOk;
+  const int32_t P = plan_.P, R = plan_.R;
+  std::vector<uint8_t> global(P, 0);
+  for (int32_t r = 0; r < R; ++r)
+    for (int32_t v = 0; v < P; ++v) global[v] |= used_acc_[static_cast<size_t>(r) * P + v];
+  int rc = launcher_->set_used(used_acc_.data(), global.data(), err);
+  if (rc != kOk) return rc;
+  for (int32_t v = 0; v < P; ++v) {
+    if (global[v]) continue;
+    ready_[v] = 1;
+    --pending_[plan_.loc[v].bucket];
+  }
+  return launch_ready(call, err);
+}
+
+int Reducer::set_local_used(const uint8_t* used, std::string* err) {
+  if (iteration_open()) {
+    *err = "set_local_used: must come before the iteration's hooks";
+    return kErrState;
+  }
+  const size_t n = static_cast<size_t>(plan_.R) * plan_.P;
+  if (!used_set_) used_acc_.assign(n, 0);
+  // [Li] "Gradient Accumulation (no_sync)": under no_sync the flags of the
+  // local steps accumulate (OR) until the next synchronisation.
+  for (size_t i = 0; i < n; ++i) used_acc_[i] |= used ? (used[i] ? 1 : 0) : 1;
+  used_set_ = true;
   return kOk;
 }
 
@@ -195,6 +234,11 @@ int Reducer::finalize(std::string* err) {
     return kErrState;
   }
   if (!sync_ && calls_ == 0) return kOk;
+  if (!failed_ && calls_ == 0) {          // no hook fired: only unused variables, if any
+    log_.clear();
+    const int rc = mark_unused_ready(0, err);
+    if (rc != kOk) return rc;
+  }
   if (failed_ || next_bucket_ != plan_.B()) {
     failed_ = true;
     *err = "finalize: not every bucket was reduced in this iteration (" +
@@ -205,8 +249,15 @@ int Reducer::finalize(std::string* err) {
   // every bucket's reduction, without a host synchronization.
   const int rc = launcher_->join(err);
   log_ring_[finalized_ % kTimeRing] = log_;
-  last_order_ = order_now_;
-  has_order_ = true;
+  // a rebuild needs every variable's place in the ready order ([C30]: no
+  // ready-order rebuild when the set of used parameters changes)
+  has_order_ = (static_cast<int32_t>(order_now_.size()) == plan_.P);
+  if (has_order_) last_order_ = order_now_;
+  if (used_set_) {                        // the flags served this synchronisation
+    used_set_ = false;
+    std::string e2;
+    launcher_->set_used(nullptr, nullptr, &e2);
+  }
   ++finalized_;
   begin_iteration();
   return rc;

@@ -131,6 +131,10 @@ class Launcher {
   virtual int clock_hz(int64_t* hz, std::string* err) = 0;
   // Caps the workgroups of each reduction launch (0 = one per four segments).
   virtual void set_max_blocks(int32_t n) = 0;
+  // Used flags for the launches that follow (R * P replica-major, and the OR
+  // over replicas per variable), or NULL for "all used". Ordered on the
+  // compute stream before the next launch's ready event.
+  virtual int set_used(const uint8_t* used, const uint8_t* global, std::string* err) = 0;
 };
 
 std::unique_ptr<Launcher> make_launcher();
@@ -152,6 +156,9 @@ class Reducer {
   // [C30] "第一次迭代为何不同": re-plan from the hook order of the last finished
   // iteration (same cap rule); the handle must be bound again afterwards.
   int rebuild_buckets(int64_t cap_bytes, std::string* err);
+  // Per-replica used flags (R * P, replica-major; NULL = all used) for the
+  // coming synchronisation; OR-ed with earlier calls since the last sync.
+  int set_local_used(const uint8_t* used, std::string* err);
   const std::vector<int32_t>& last_ready_order() const { return last_order_; }
   const std::vector<LaunchRecord>& log() const { return log_; }
   int64_t finalized() const { return finalized_; }
@@ -176,6 +183,11 @@ class Reducer {
   std::vector<int32_t> order_now_;   // hook order of the current iteration
   std::vector<int32_t> last_order_;  // ... of the last finished iteration
   bool has_order_ = false;
+  std::vector<uint8_t> used_acc_;    // R * P used flags, OR-ed until the next sync
+  bool used_set_ = false;
+
+  int launch_ready(int32_t call, std::string* err);
+  int mark_unused_ready(int32_t call, std::string* err);
   int64_t finalized_ = 0;          // iterations finalized so far
   std::vector<LaunchRecord> log_ring_[kTimeRing];
 };

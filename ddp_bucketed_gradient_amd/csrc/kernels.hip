@@ -10,7 +10,7 @@
 // once with 128-bit accesses and does a handful of adds per element.
 //
 // Work decomposition: the host cuts every bucket member into segments of at
-// most 4096 elements (core.cpp). One wavefront owns one segment; a workgroup
+// most kSegElems (8192) elements (core.cpp). One wavefront owns one segment; a workgroup
 // of 256 threads owns four consecutive segments. Each lane moves v4fs at
 // lane stride, so one instruction covers 1 KiB of contiguous memory per
 // replica, and it issues all R (x unroll) loads before the first add to keep
@@ -24,6 +24,10 @@
 //                       grid-stride over contiguous v4fs.
 //   copyback_kernel     staged step 3: averaged bucket -> R gradients.
 //   accumulate_kernel   no_sync: grad (+)= float(step) for every replica.
+//   zero_unused_kernel  bucket views: zero the slices of unused variables.
+//
+// With used flags (unused parameters) the copy-mode kernels skip variables no
+// replica used and read zeros for replicas that did not use a variable.
 //
 // Short page names are defined in core.hpp.
 #include <hip/hip_ext.h>
@@ -137,12 +141,24 @@ struct Unroll {
 // ---------------------------------------------------------------------------
 // fused gather + mean + copy-back, one wavefront per segment
 
+// Which replicas contribute to variable `var` (bit r), from the R x P used
+// flags; all replicas when there are no flags.
+template <typename M>
+__device__ __forceinline__ M used_mask(const uint8_t* used, int32_t var, int32_t P, int R) {
+  if (used == nullptr) return R >= static_cast<int>(sizeof(M) * 8) ? ~M(0) : ((M(1) << R) - 1);
+  M m = 0;
+  for (int r = 0; r < R; ++r) m |= static_cast<M>(used[static_cast<int64_t>(r) * P + var] ? 1 : 0) << r;
+  return m;
+}
+
 template <int R>
 __global__ __launch_bounds__(kBlock) void fused_mean_kernel(const Segment* __restrict__ segs, int32_t nseg,
                                                             float* const* __restrict__ grads, int32_t P,
                                                             float scale, int32_t vec_ok,
+                                                            const uint8_t* __restrict__ used,
                                                             int64_t* __restrict__ stamp) {
   constexpr int U = Unroll<R>::value;
+  constexpr uint32_t kAll = (1u << R) - 1;
   stamp_begin(stamp);
   // One wavefront per segment; with a capped grid (fewer workgroups than
   // segments / 4) each wavefront strides over the remaining segments.
@@ -152,10 +168,28 @@ __global__ __launch_bounds__(kBlock) void fused_mean_kernel(const Segment* __res
     float* p[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) p[r] = grads[static_cast<int64_t>(r) * P + g.var] + g.start;
+    const int lane = lane_id();
+    const uint32_t mask = used_mask<uint32_t>(used, g.var, P, R);
+    if (mask == 0) continue;                 // no replica used it: leave every gradient untouched
+    if (mask != kAll) {
+      // Some replicas did not use this variable: their bucket slice is zero,
+      // so they add +0.0 in their place of the fixed order.
+      for (int j = lane; j < len; j += 64) {
+        float x[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) x[r] = ((mask >> r) & 1u) ? G(p[r])[j] : 0.0f;
+        float a = x[0];
+#pragma unroll
+        for (int r = 1; r < R; ++r) a = a + x[r];
+        const float m = finish<R>(a, scale);
+#pragma unroll
+        for (int r = 0; r < R; ++r) G(p[r])[j] = m;
+      }
+      continue;
+    }
     uintptr_t any = 0;                       // 16-byte alignment of every replica's pointer
 #pragma unroll
     for (int r = 0; r < R; ++r) any |= reinterpret_cast<uintptr_t>(p[r]);
-    const int lane = lane_id();
     int tail = 0;
     if (vec_ok && (g.flags & kSegVecStart) && (any & 15) == 0) {
       const int n4 = len >> 2;
@@ -205,6 +239,7 @@ __global__ __launch_bounds__(kBlock) void fused_mean_kernel(const Segment* __res
 __global__ __launch_bounds__(kBlock) void fused_mean_kernel_rt(const Segment* __restrict__ segs, int32_t nseg,
                                                                float* const* __restrict__ grads, int32_t P,
                                                                int32_t R, float scale, int32_t pow2,
+                                                               const uint8_t* __restrict__ used,
                                                                int64_t* __restrict__ stamp) {
   stamp_begin(stamp);
   // One wavefront per segment; with a capped grid (fewer workgroups than
@@ -212,9 +247,12 @@ __global__ __launch_bounds__(kBlock) void fused_mean_kernel_rt(const Segment* __
   for (int s = blockIdx.x * kWavesPerBlock + wave_id(); s < nseg; s += gridDim.x * kWavesPerBlock) {
     const Segment g = segs[s];
     const int len = static_cast<int>(g.len);
+    const uint64_t mask = used_mask<uint64_t>(used, g.var, P, R);
+    if (mask == 0) continue;
     for (int j = lane_id(); j < len; j += 64) {
-      float a = G(grads[g.var])[g.start + j];
-      for (int r = 1; r < R; ++r) a = a + G(grads[static_cast<int64_t>(r) * P + g.var])[g.start + j];
+      float a = (mask & 1u) ? G(grads[g.var])[g.start + j] : 0.0f;
+      for (int r = 1; r < R; ++r)
+        a = a + (((mask >> r) & 1u) ? G(grads[static_cast<int64_t>(r) * P + g.var])[g.start + j] : 0.0f);
       const float m = finish_rt(a, R, scale, pow2 != 0);
       for (int r = 0; r < R; ++r) G(grads[static_cast<int64_t>(r) * P + g.var])[g.start + j] = m;
     }
@@ -230,7 +268,9 @@ __global__ __launch_bounds__(kBlock) void fused_mean_kernel_rt(const Segment* __
 __global__ __launch_bounds__(kBlock) void pack_kernel(const Segment* __restrict__ segs, int32_t nseg,
                                                       float* const* __restrict__ grads, int32_t P, int32_t R,
                                                       float* __restrict__ flat, int64_t flat_stride,
-                                                      int64_t fbase, int32_t vec_ok, int64_t* __restrict__ stamp) {
+                                                      int64_t fbase, int32_t vec_ok,
+                                                      const uint8_t* __restrict__ used,
+                                                      int64_t* __restrict__ stamp) {
   stamp_begin(stamp);
   // One wavefront per segment; with a capped grid (fewer workgroups than
   // segments / 4) each wavefront strides over the remaining segments.
@@ -242,6 +282,10 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(const Segment* __restrict_
     for (int r = 0; r < R; ++r) {
       const float* src = grads[static_cast<int64_t>(r) * P + g.var] + g.start;
       float* dst = flat + r * flat_stride + fbase + g.boff;
+      if (used != nullptr && !used[static_cast<int64_t>(r) * P + g.var]) {
+        for (int j = lane; j < len; j += 64) G(dst)[j] = 0.0f;   // unused here: zero slice
+        continue;
+      }
       int tail = 0;
       if (vec && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
         const int n4 = len >> 2;
@@ -299,12 +343,14 @@ __global__ __launch_bounds__(kBlock) void mean_kernel_rt(const float* __restrict
 __global__ __launch_bounds__(kBlock) void copyback_kernel(const Segment* __restrict__ segs, int32_t nseg,
                                                           float* const* __restrict__ grads, int32_t P, int32_t R,
                                                           const float* __restrict__ avg, int64_t fbase,
-                                                          int32_t vec_ok, int64_t* __restrict__ stamp) {
+                                                          int32_t vec_ok, const uint8_t* __restrict__ used,
+                                                          int64_t* __restrict__ stamp) {
   stamp_begin(stamp);
   // One wavefront per segment; with a capped grid (fewer workgroups than
   // segments / 4) each wavefront strides over the remaining segments.
   for (int s = blockIdx.x * kWavesPerBlock + wave_id(); s < nseg; s += gridDim.x * kWavesPerBlock) {
     const Segment g = segs[s];
+    if (used_mask<uint64_t>(used, g.var, P, R) == 0) continue;   // globally unused: untouched
     const int len = static_cast<int>(g.len);
     const int lane = lane_id();
     const float* src = avg + fbase + g.boff;
@@ -350,6 +396,11 @@ __global__ __launch_bounds__(kBlock) void accumulate_kernel(const Segment* __res
   const int64_t k = static_cast<int64_t>(r) * P + g.var;
   float* acc = grads[k] + g.start;
   const int lane = lane_id();
+  if (steps[k] == nullptr) {                 // no gradient from this replica in this micro-step
+    if (FIRST)
+      for (int j = lane; j < len; j += 64) G(acc)[j] = 0.0f;
+    return;
+  }
   int tail = 0;
   if (BF16) {
     const uint16_t* st = static_cast<const uint16_t*>(steps[k]) + g.start;
@@ -426,6 +477,24 @@ __global__ __launch_bounds__(kBlock) void accumulate_kernel(const Segment* __res
   }
 }
 
+// gradient_as_bucket_view with unused parameters ([Li] "Handling Unused
+// Parameters"): the view of a variable a replica did not use is its slice of
+// the bucket, which must read as zeros. One wavefront per (segment, replica).
+__global__ __launch_bounds__(kBlock) void zero_unused_kernel(const Segment* __restrict__ segs, int32_t nseg,
+                                                             float* const* __restrict__ grads,
+                                                             const uint8_t* __restrict__ used, int32_t P,
+                                                             int32_t R) {
+  const int64_t w = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave_id();
+  if (w >= static_cast<int64_t>(nseg) * R) return;
+  const int r = static_cast<int>(w / nseg);
+  const Segment g = segs[w - static_cast<int64_t>(r) * nseg];
+  const int64_t k = static_cast<int64_t>(r) * P + g.var;
+  if (used[k]) return;
+  float* dst = grads[k] + g.start;
+  const int len = static_cast<int>(g.len);
+  for (int j = lane_id(); j < len; j += 64) G(dst)[j] = 0.0f;
+}
+
 // ---------------------------------------------------------------------------
 // launcher
 
@@ -469,6 +538,11 @@ class HipLauncher final : public Launcher {
     HIP_OK(hipMalloc(&d_steps_, std::max<size_t>(nptr, 1) * kStepSlots * sizeof(void*)), "hipMalloc(step tables)");
     HIP_OK(hipHostMalloc(&h_steps_, std::max<size_t>(nptr, 1) * kStepSlots * sizeof(void*), hipHostMallocDefault),
            "hipHostMalloc(step staging)");
+    HIP_OK(hipMalloc(&d_used_, std::max<size_t>(nptr, 1)), "hipMalloc(used flags)");
+    HIP_OK(hipHostMalloc(&h_used_, std::max<size_t>(nptr, 1), hipHostMallocDefault), "hipHostMalloc(used staging)");
+    HIP_OK(hipEventCreateWithFlags(&ev_used_, hipEventDisableTiming), "hipEventCreate");
+    used_recorded_ = false;
+    used_active_ = false;
     if (nptr)
       HIP_OK(hipMemcpyAsync(d_grads_, a.grad_ptrs.data(), nptr * sizeof(float*), hipMemcpyHostToDevice, compute_),
              "upload pointer table");
@@ -549,12 +623,6 @@ class HipLauncher final : public Launcher {
     const size_t nptr = static_cast<size_t>(R_) * P_;
     if (plan_->segs.empty()) return kOk;
     const int vec = vec_ok_;       // alignment is checked per segment in the kernel
-    for (size_t i = 0; i < nptr; ++i) {
-      if (step_ptrs[i] == nullptr && plan_->numel[i % P_] > 0) {
-        *err = "no_sync_accumulate: NULL step pointer";
-        return kErrArg;
-      }
-    }
     // Step pointer tables go through a small ring of device slots; a table
     // seen recently is reused without another upload.
     int slot = -1;
@@ -631,6 +699,34 @@ class HipLauncher final : public Launcher {
 
   void set_max_blocks(int32_t n) override { max_blocks_ = n; }
 
+  int set_used(const uint8_t* used, const uint8_t* global, std::string* err) override {
+    (void)global;                  // the kernels derive it from the per-replica flags
+    if (used == nullptr) {
+      used_active_ = false;
+      return kOk;
+    }
+    const size_t n = static_cast<size_t>(R_) * P_;
+    if (n == 0) return kOk;
+    // The staging buffer may still feed the previous upload.
+    if (used_recorded_) HIP_OK(hipEventSynchronize(ev_used_), "hipEventSynchronize(used)");
+    std::memcpy(h_used_, used, n);
+    HIP_OK(hipMemcpyAsync(d_used_, h_used_, n, hipMemcpyHostToDevice, compute_), "upload used flags");
+    HIP_OK(hipEventRecord(ev_used_, compute_), "hipEventRecord(used)");
+    used_recorded_ = true;
+    used_active_ = true;
+    // Bucket views: zero the slices of unused (replica, variable) pairs on the
+    // compute stream, ahead of every ready event of this iteration.
+    if (mode_ == kModeBucketView && !plan_->segs.empty() && std::memchr(used, 0, n) != nullptr) {
+      const int32_t nseg = static_cast<int32_t>(plan_->segs.size());
+      const int64_t waves = static_cast<int64_t>(nseg) * R_;
+      const dim3 grid(static_cast<unsigned>((waves + kWavesPerBlock - 1) / kWavesPerBlock));
+      hipLaunchKernelGGL(zero_unused_kernel, grid, dim3(kBlock), 0, compute_, d_segs_, nseg, d_grads_, d_used_, P_,
+                         R_);
+      HIP_OK(hipGetLastError(), "launch zero_unused_kernel");
+    }
+    return kOk;
+  }
+
   int clock_hz(int64_t* hz, std::string* err) override {
     int dev = 0, khz = 0;
     HIP_OK(hipGetDevice(&dev), "hipGetDevice");
@@ -655,6 +751,7 @@ class HipLauncher final : public Launcher {
     const Segment* segs = (view ? d_view_segs_ : d_segs_) + s0;
     float* const* table = view ? d_view_bases_ : d_grads_;
     const int32_t tp = view ? 1 : P_;
+    const uint8_t* used = (used_active_ && !view) ? d_used_ : nullptr;   // views were zeroed at the first hook
     int64_t* stamp = (flags_ & 1) ? d_stamps_ + static_cast<int64_t>(b) * 4 : nullptr;
     int64_t blocks = (nseg + kWavesPerBlock - 1) / kWavesPerBlock;
     if (max_blocks_ > 0) blocks = std::min<int64_t>(blocks, max_blocks_);
@@ -665,7 +762,7 @@ class HipLauncher final : public Launcher {
 #define DDPB_FUSED_CASE(RR)                                                                                      \
   case RR:                                                                                                       \
     hipExtLaunchKernelGGL((fused_mean_kernel<RR>), grid, block, 0, s, t0, t1, 0, segs, nseg, table, tp, scale_,   \
-                          vec_ok_, stamp);                                                                       \
+                          vec_ok_, used, stamp);                                                                 \
     break;
         DDPB_FUSED_CASE(1) DDPB_FUSED_CASE(2) DDPB_FUSED_CASE(3) DDPB_FUSED_CASE(4)
         DDPB_FUSED_CASE(5) DDPB_FUSED_CASE(6) DDPB_FUSED_CASE(7) DDPB_FUSED_CASE(8)
@@ -674,7 +771,7 @@ class HipLauncher final : public Launcher {
 #undef DDPB_FUSED_CASE
         default:
           hipExtLaunchKernelGGL(fused_mean_kernel_rt, grid, block, 0, s, t0, t1, 0, segs, nseg, table, tp, R_,
-                                scale_, pow2_ ? 1 : 0, stamp);
+                                scale_, pow2_ ? 1 : 0, used, stamp);
       }
       HIP_OK(hipGetLastError(), "launch fused_mean_kernel");
       return kOk;
@@ -684,7 +781,7 @@ class HipLauncher final : public Launcher {
     const int64_t n = plan_->bucket_elems[b];
     const int64_t stride = plan_->flat_elems;
     hipExtLaunchKernelGGL(pack_kernel, grid, block, 0, s, t0, nullptr, 0, segs, nseg, d_grads_, P_, R_, flat_, stride,
-                          fbase, vec_ok_, stamp);
+                          fbase, vec_ok_, used, stamp);
     HIP_OK(hipGetLastError(), "launch pack_kernel");
     const int64_t n4 = std::max<int64_t>(n >> 2, 1);
     int64_t mblocks = std::min<int64_t>((n4 + kBlock - 1) / kBlock, 2048);
@@ -706,7 +803,7 @@ class HipLauncher final : public Launcher {
     }
     HIP_OK(hipGetLastError(), "launch mean_kernel");
     hipExtLaunchKernelGGL(copyback_kernel, grid, block, 0, s, nullptr, t1, 0, segs, nseg, d_grads_, P_, R_, avg_,
-                          fbase, vec_ok_, static_cast<int64_t*>(nullptr));
+                          fbase, vec_ok_, used, static_cast<int64_t*>(nullptr));
     HIP_OK(hipGetLastError(), "launch copyback_kernel");
     return kOk;
   }
@@ -731,6 +828,14 @@ class HipLauncher final : public Launcher {
     d_view_bases_ = nullptr;
     d_view_segs_ = nullptr;
     if (h_steps_) (void)hipHostFree(h_steps_);
+    if (ev_used_) (void)hipEventDestroy(ev_used_);
+    if (d_used_) (void)hipFree(d_used_);
+    if (h_used_) (void)hipHostFree(h_used_);
+    ev_used_ = nullptr;
+    d_used_ = nullptr;
+    h_used_ = nullptr;
+    used_active_ = false;
+    used_recorded_ = false;
     d_grads_ = nullptr;
     d_segs_ = nullptr;
     d_stamps_ = nullptr;
@@ -755,6 +860,11 @@ class HipLauncher final : public Launcher {
   float** d_view_bases_ = nullptr;
   Segment* d_view_segs_ = nullptr;
   void** h_steps_ = nullptr;
+  uint8_t* d_used_ = nullptr;   // R x P used flags of the coming synchronisation
+  uint8_t* h_used_ = nullptr;   // pinned staging for their upload
+  hipEvent_t ev_used_ = nullptr;
+  bool used_recorded_ = false;
+  bool used_active_ = false;
   float* flat_ = nullptr;
   float* avg_ = nullptr;
   std::vector<hipEvent_t> ev_ready_, ev_done_, ev_slot_, ev_t0_, ev_t1_;

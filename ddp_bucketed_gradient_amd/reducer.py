@@ -152,9 +152,12 @@ class Reducer:
         self.lib.finalize(h)
 
     def no_sync_accumulate(self, steps, first_step: bool):
-        """steps[r][v]: contiguous fp32 or bf16 CUDA tensor per replica/variable."""
+        """steps[r][v]: contiguous fp32 or bf16 CUDA tensor per replica/variable,
+        or None where that replica produced no gradient (zeros on the first
+        step, unchanged afterwards)."""
         import torch
-        dt = steps[0][0].dtype
+        present = [t for row in steps for t in row if t is not None]
+        dt = present[0].dtype if present else torch.float32
         code = {torch.float32: F32, torch.bfloat16: BF16}.get(dt)
         if code is None:
             raise ValueError("step gradients must be fp32 or bf16")
@@ -162,10 +165,26 @@ class Reducer:
         for r in range(self.R):
             for v in range(self.P):
                 t = steps[r][v]
+                if t is None:
+                    ptrs.append(0)
+                    continue
                 if t.dtype != dt or not t.is_contiguous():
                     raise ValueError("step gradients must be contiguous and of one dtype")
                 ptrs.append(t.data_ptr())
         self.lib.no_sync_accumulate(self.h, ptrs, code, first_step)
+
+    def set_local_used(self, used):
+        """Which replicas use which variables in the coming backward pass: an
+        R x P array-like of booleans (or None for all used). Calls before one
+        synchronisation OR together."""
+        if used is None:
+            self.lib.set_local_used(self.h, None)
+            return
+        import numpy as np
+        u = np.asarray(used, dtype=bool)
+        if u.shape != (self.R, self.P):
+            raise ValueError(f"used flags must have shape ({self.R}, {self.P})")
+        self.lib.set_local_used(self.h, u.astype(np.uint8).ravel().tolist())
 
     # -- diagnostics -------------------------------------------------------------------
     def launch_log(self, with_stamps: bool = False):

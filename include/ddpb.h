@@ -226,10 +226,33 @@ int ddpb_set_sync(ddpb_t h, int32_t enabled);
 /* Local gradient accumulation of one backward pass into the bound fp32
  * gradients, on the compute stream: grad = float(step) when first_step != 0,
  * grad += float(step) otherwise, elementwise for every replica and variable.
- *   step_ptrs   R*P device pointers (replica-major), numel[v] elements each
+ *   step_ptrs   R*P device pointers (replica-major), numel[v] elements each;
+ *               NULL = that replica produced no gradient for the variable in
+ *               this backward (zeros on the first step, unchanged otherwise)
  *   step_dtype  DDPB_F32 or DDPB_BF16 (widened exactly to fp32) */
 int ddpb_no_sync_accumulate(ddpb_t h, void* const* step_ptrs, int32_t step_dtype,
                             int32_t first_step);
+
+/* Unused parameters ([Li] "Handling Unused Parameters and Sub-Graph
+ * Execution"; [TP] "When a parameter never receives a gradient"; [C30]
+ * "Unused Parameter"): which replicas will produce a gradient for which
+ * variables in the coming backward pass, as the forward's graph walk finds
+ * them.
+ *   used   R*P host bytes, replica-major (used[r*P + v] != 0: replica r uses
+ *          variable v), read before the call returns; NULL = all used
+ * Calls before one synchronisation OR together (no_sync micro-steps each add
+ * their flags); the flags serve the next synchronising iteration and are then
+ * dropped. At that iteration's first ddpb_mark_ready (or at ddpb_finalize when
+ * no hook fires), variables no replica used count as ready, so their buckets
+ * can complete; they must not be marked again (DDPB_E_DOUBLE_READY). In the
+ * reduction a replica that did not use a variable contributes zeros, and a
+ * variable that no replica used keeps every replica's gradient untouched
+ * (copy modes). With bucket views the unused views are zeroed on the compute
+ * stream at that first hook and then averaged with their bucket, so a
+ * globally unused view ends as zeros. An iteration with unused variables
+ * records no ready order for ddpb_rebuild_buckets. DDPB_E_STATE if an
+ * iteration is in progress. */
+int ddpb_set_local_used(ddpb_t h, const uint8_t* used);
 
 /* Clears a latched DDPB_E_INCOMPLETE and the per-iteration state. Buckets
  * already enqueued keep running. */

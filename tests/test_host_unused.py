@@ -1,0 +1,126 @@
+"""CPU tests of the native unused-parameter handling (host-only build) against
+the oracle: the same buckets launch at the same hook calls, documented errors,
+and the flags OR over no_sync steps and are dropped after a synchronisation."""
+import os
+
+import numpy as np
+import pytest
+
+import ddp_bucketed_gradient_amd as D
+from ddp_bucketed_gradient_amd import _abi
+from oracle import reducer as OR
+from workloads import gen as WG
+
+
+@pytest.fixture(scope="module")
+def host():
+    if not os.path.exists(D.HOSTONLY_LIB):
+        from ddp_bucketed_gradient_amd import build
+        build.build_hostonly()
+    return D.Lib(D.HOSTONLY_LIB)
+
+
+def _pair(host, numels, R, cap):
+    red = D.Reducer([(n,) for n in numels], R, cap, lib=host)
+    red.bind_ptrs([0x1000 + 16 * i for i in range(R * len(numels))], side_streams=[0])
+    orc = OR.Reducer(numels, R, cap)
+    orc.bind([[np.zeros(n, np.float32) for n in numels] for _ in range(R)])
+    return red, orc
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_launches_match_oracle_with_unused(host, seed):
+    rng = np.random.default_rng(seed)
+    P = int(rng.integers(1, 40))
+    R = int(rng.integers(1, 6))
+    numels = WG.random_numels(seed, P, 0, 300)
+    cap = int(rng.integers(0, 4 * sum(numels) + 1))
+    red, orc = _pair(host, numels, R, cap)
+    for it in range(3):                             # flags change from iteration to iteration
+        used = rng.random((R, P)) < (0.3 + 0.3 * it)
+        G = used.any(axis=0)
+        order = [v for v in WG.permutation(seed * 10 + it, P) if G[v]]
+        red.set_local_used(used)
+        orc.set_local_used(used)
+        orc.launch_log.clear()
+        red.sync(order)
+        orc.sync(order)
+        assert red.launch_log() == orc.launch_log, it
+
+
+def test_unused_variable_marked_again_is_double_ready(host):
+    red, _ = _pair(host, [4, 4, 4], 2, 0)
+    red.set_local_used([[True, False, True], [True, False, True]])
+    red.mark_ready(2)                               # first hook: variable 1 counts as ready
+    with pytest.raises(D.DdpbError) as e:
+        red.mark_ready(1)
+    assert e.value.code == _abi.E_DOUBLE_READY
+
+
+def test_flags_only_between_iterations(host):
+    red, _ = _pair(host, [4, 4], 2, 0)
+    red.mark_ready(1)
+    with pytest.raises(D.DdpbError) as e:
+        red.set_local_used([[True, True], [True, True]])
+    assert e.value.code == _abi.E_STATE
+    red.mark_ready(0)
+    red.finalize()
+
+
+def test_all_unused_finishes_at_finalize(host):
+    red, orc = _pair(host, [4, 5, 6], 2, 4 * 5)
+    flags = np.zeros((2, 3), bool)
+    red.set_local_used(flags)
+    orc.set_local_used(flags)
+    red.finalize()
+    orc.finalize()
+    assert red.launch_log() == orc.launch_log == [(b, 0) for b in range(red.num_buckets)]
+
+
+def test_skipping_without_flags_fails(host):
+    red, _ = _pair(host, [4, 4, 4], 2, 0)
+    red.mark_ready(2)
+    red.mark_ready(1)
+    with pytest.raises(D.DdpbError) as e:
+        red.finalize()
+    assert e.value.code == _abi.E_INCOMPLETE
+    red.reset()
+
+
+def test_flags_dropped_after_synchronisation(host):
+    red, orc = _pair(host, [4, 4], 2, 0)
+    red.set_local_used([[True, False], [True, False]])
+    red.sync([0])
+    with pytest.raises(D.DdpbError) as e:           # next iteration: every variable is expected again
+        red.sync([0])
+    assert e.value.code == _abi.E_INCOMPLETE
+    red.reset()
+
+
+def test_flags_or_over_no_sync_steps(host):
+    numels = [5, 7, 3]
+    red, orc = _pair(host, numels, 2, 0)
+    red.set_sync(False)
+    red.set_local_used([[True, False, False], [True, False, False]])
+    red.sync([0])                                   # hooks are no-ops under no_sync
+    red.set_sync(True)
+    red.set_local_used([[True, False, False], [False, True, False]])
+    orc.set_local_used([[True, True, False], [True, True, False]])
+    red.sync([1, 0])
+    orc.sync([1, 0])
+    assert red.launch_log() == orc.launch_log       # variable 2 unused: its bucket launched at the first hook
+
+
+def test_rebuild_refused_after_unused_iteration(host):
+    red, _ = _pair(host, [4, 4, 4], 2, 0)
+    red.set_local_used([[True, False, True]] * 2)
+    red.sync([2, 0])
+    with pytest.raises(D.DdpbError) as e:
+        red.rebuild_buckets(0)
+    assert e.value.code == _abi.E_STATE
+
+
+def test_flag_shape_checked(host):
+    red, _ = _pair(host, [4, 4], 2, 0)
+    with pytest.raises(ValueError):
+        red.set_local_used([[True, True, True]])
