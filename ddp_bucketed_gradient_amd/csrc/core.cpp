@@ -141,7 +141,7 @@ int Reducer::bind(const BindArgs& args, std::string* err) {
 int Reducer::ensure_prior_reduction_finished(std::string* err) {
   if (failed_ || iteration_open()) {
     failed_ = true;
-    *err = "Expected to have finished reduction in the prior iteration before starting a new one";
+    *err = "the previous iteration left buckets unreduced; a new iteration cannot start before ddpb_reset";
     return kErrIncomplete;
   }
   return kOk;
@@ -158,7 +158,7 @@ int Reducer::mark_ready(int32_t v, std::string* err) {
   }
   if (!sync_) return kOk;     // no_sync: the hook runs but does nothing
   if (failed_) {
-    *err = "Expected to have finished reduction in the prior iteration before starting a new one";
+    *err = "the previous iteration left buckets unreduced; a new iteration cannot start before ddpb_reset";
     return kErrIncomplete;
   }
   if (calls_ == 0) {

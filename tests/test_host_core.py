@@ -211,7 +211,7 @@ def test_unfinished_iteration_detected_before_next_forward(host):
     _bind_fake(red)
     red.mark_ready(1)
     assert _code(red.ensure_prior_reduction_finished) == _abi.E_INCOMPLETE
-    assert "Expected to have finished reduction in the prior iteration" in host.last_error()
+    assert "previous iteration left buckets unreduced" in host.last_error()
 
 
 def test_create_argument_errors(host):
