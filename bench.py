@@ -136,6 +136,7 @@ def cpu_baseline_sync(w, host_in, nvars_sample, sample_bytes, min_seconds):
     red = OR.Reducer(sub, w.R, w.cap_bytes)
     grads = [[host_in[v][r].copy() for v in range(first_v, P)] for r in range(w.R)]
     red.bind(grads)
+    red.sync()                       # untimed: first touch of the oracle's bucket buffers
     reps = 0
     t0 = time.perf_counter()
     while True:                      # whole syncs until about min_seconds of CPU work
@@ -146,6 +147,44 @@ def cpu_baseline_sync(w, host_in, nvars_sample, sample_bytes, min_seconds):
             break
     gbs = 2 * w.R * sample_bytes * reps / dt / 1e9
     return gbs, dt, red.B, reps
+
+
+def cpu_baseline_threads(w, host_in, nvars_sample, min_seconds, threads):
+    """The same oracle on the same sample, its variables dealt round-robin (by
+    size) to `threads` independent oracle reducers that run concurrently (NumPy
+    releases the GIL inside its array operations). Values are elementwise, so
+    the split changes no result, only which thread computes it."""
+    import threading
+    from oracle import reducer as OR
+    numels = w.numels()
+    P = len(numels)
+    vs = sorted(range(P - nvars_sample, P), key=lambda v: -numels[v])
+    groups = [g for g in (vs[i::threads] for i in range(threads)) if g]
+    reds = []
+    for g in groups:
+        red = OR.Reducer([numels[v] for v in g], w.R, w.cap_bytes)
+        red.bind([[host_in[v][r].copy() for v in g] for r in range(w.R)])
+        red.sync()                   # untimed, as in the single-thread figure
+        reds.append(red)
+    reps = [0] * len(reds)
+    stop = threading.Event()
+
+    def work(i):
+        while not stop.is_set():
+            reds[i].sync()
+            reps[i] += 1
+
+    ths = [threading.Thread(target=work, args=(i,)) for i in range(len(reds))]
+    t0 = time.perf_counter()
+    for t in ths:
+        t.start()
+    time.sleep(min_seconds)
+    stop.set()
+    for t in ths:
+        t.join()
+    dt = time.perf_counter() - t0
+    done = sum(2 * w.R * 4 * sum(numels[v] for v in g) * n for g, n in zip(groups, reps))
+    return done / dt / 1e9, dt, len(reds), min(reps)
 
 
 def run_sync_bench(args, torch, D, WG, WC):
@@ -189,6 +228,7 @@ def run_sync_bench(args, torch, D, WG, WC):
 
     # snapshot of the oracle's sample (first buckets), before any sync
     cpu = None
+    cpu_threads = None
     host_in = None
     nvars_sample = 0
     sample_bytes = 0
@@ -209,21 +249,24 @@ def run_sync_bench(args, torch, D, WG, WC):
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps)")
 
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one event on the compute stream before each sync and after the last: the
+    # interval between consecutive events is one sync (from the previous join
+    # to this sync's join), for the median and p95
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     per_step = []                       # (starts, durations) of every launch, per step
     ring = 64                           # iterations whose launch events the library keeps
     read = 0                            # timed steps whose launch times were collected
     torch.cuda.synchronize()            # barrier (one process) + device sync
     t0 = time.perf_counter()
-    ev0.record(compute)
+    evs[0].record(compute)
     for k in range(args.steps):
         red.sync(order)
+        evs[k + 1].record(compute)
         # Collect launch times of steps that are about to leave the library's
         # ring, well behind the device, so the host never waits on recent work.
         while flags and k - read >= ring - 8:
             per_step.append(red.launch_times_ms(k - read, True))
             read += 1
-    ev1.record(compute)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     while flags and read < args.steps:
@@ -232,7 +275,11 @@ def run_sync_bench(args, torch, D, WG, WC):
     launch_ms = [d for _, ds in per_step for d in ds]
     busy_ms = sum(union_length(st, ds) for st, ds in per_step)
     wall_ms = (t1 - t0) * 1e3 / args.steps
-    ev_ms = ev0.elapsed_time(ev1) / args.steps
+    ev_ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    sync_ms = sorted(evs[k].elapsed_time(evs[k + 1]) for k in range(args.steps))
+    half = len(sync_ms) // 2
+    med_ms = sync_ms[half] if len(sync_ms) % 2 else 0.5 * (sync_ms[half - 1] + sync_ms[half])
+    p95_ms = sync_ms[-(-95 * len(sync_ms) // 100) - 1]      # nearest rank
     log(f"timed {args.steps} steps: {wall_ms:.3f} ms/step wall, {ev_ms:.3f} ms/step events")
 
     alg = 2 * R * S
@@ -265,6 +312,13 @@ def run_sync_bench(args, torch, D, WG, WC):
                "sample": f"{w.name}: first {nb} of {B} buckets ({nvars_sample} tensors, "
                          f"{sample_bytes / 1e6:.1f} MB per replica, R={R}) from the same device inputs; "
                          f"NumPy single thread, {reps} sync(s) in {dt:.1f} s"}
+        nthr = max(1, min(16, len(os.sched_getaffinity(0))))
+        if nthr > 1:
+            log(f"timing the oracle on the same sample in {nthr} threads")
+            gbs_t, dt_t, ng, reps_t = cpu_baseline_threads(w, host_in, nvars_sample, args.cpu_min_seconds, nthr)
+            cpu_threads = {"value": round(gbs_t, 3), "unit": "GB/s", "cores": ng, "kind": "oracle",
+                           "sample": f"same sample, its tensors dealt to {ng} oracle reducers in threads; "
+                                     f"at least {reps_t} sync(s) each in {dt_t:.1f} s"}
         del host_in
 
     copy_gbps = hbm_copy_ceiling(torch)
@@ -288,8 +342,11 @@ def run_sync_bench(args, torch, D, WG, WC):
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "hbm_copy_GBps": round(copy_gbps, 1),
         "ms_per_step_events": round(ev_ms, 4),
+        "ms_per_sync_median": round(med_ms, 4),
+        "ms_per_sync_p95": round(p95_ms, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "cpu_baseline_threads": cpu_threads,
     }
     return out
 
@@ -453,6 +510,23 @@ def run_overlap_bench(args, torch, D, WG, WC):
         log(f"launch_blocks={mb}: reduction {t_red:.3f} ms alone, both {t_both:.3f} ms, hidden {hidden:.3f}")
     best = min(sweep, key=lambda k: sweep[k]["t_both_ms"])
     b = sweep[best]
+    # Control: one bucket (cap above S) can only launch after the last hook,
+    # so nothing overlaps and the hidden fraction should be about 0.
+    red.set_launch_blocks(0)
+    red1 = D.Reducer([p.shape for p in params], R, 1 << 62)
+    red1.bind(grads, compute_stream=compute, side_streams=sides, flags=D.BIND_TIME_LAUNCHES)
+
+    def both1():
+        backward(red1.mark_ready)
+        red1.finalize()
+
+    t_red1 = timed(lambda: red1.sync(order), args.steps)
+    t_both1 = timed(both1, args.steps)
+    control = {"buckets": red1.num_buckets, "t_reduction_ms": round(t_red1, 4), "t_both_ms": round(t_both1, 4),
+               "hidden": round(max(0.0, min(1.0, (t_bwd + t_red1 - t_both1) / t_red1)), 4)}
+    log(f"single-bucket control: reduction {t_red1:.3f} ms alone, both {t_both1:.3f} ms, "
+        f"hidden {control['hidden']:.3f}")
+    red1.close()
     return {
         "metric": f"fraction of reduction hidden under backward; ms per step, {w.name}",
         "value": b["hidden"], "unit": "fraction", "n_gpus": 1, "steps": args.steps, "warmup": 2,
@@ -464,6 +538,7 @@ def run_overlap_bench(args, torch, D, WG, WC):
         "backward_TFLOPs": round(flops / (t_bwd * 1e-3) / 1e12, 1),
         "reduction_GBps": round(alg / (b["t_reduction_ms"] * 1e-3) / 1e9, 1),
         "launch_blocks_sweep": sweep,
+        "single_bucket_control": control,
         "roofline": None, "cpu_baseline": None,
     }
 
