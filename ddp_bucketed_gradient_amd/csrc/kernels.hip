@@ -382,12 +382,27 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);   // exact widening
 }
 
+// Unroll of the accumulation loop and whether it bypasses the caches (each
+// byte is touched once per micro-step; the accumulators of a large model do
+// not stay cached from one micro-step to the next).
+constexpr int kAccU = 8;
+constexpr bool kAccNT = true;
+
+template <bool NT>
+__device__ __forceinline__ v4f ld4x(const float* p) { if constexpr (NT) return ld4s(p); else return ld4(p); }
+template <bool NT>
+__device__ __forceinline__ void st4x(float* p, v4f v) { if constexpr (NT) st4s(p, v); else st4(p, v); }
+template <bool NT>
+__device__ __forceinline__ v2u ld2x(const uint16_t* p) {
+  if constexpr (NT) return __builtin_nontemporal_load((const gv2u*)p); else return ld2u(p);
+}
+
 template <bool BF16, bool FIRST>
 __global__ __launch_bounds__(kBlock) void accumulate_kernel(const Segment* __restrict__ segs, int32_t nseg,
                                                             float* const* __restrict__ grads,
                                                             const void* const* __restrict__ steps, int32_t P,
                                                             int32_t R, int32_t vec_ok) {
-  constexpr int U = 4;
+  constexpr int U = kAccU;
   const int64_t w = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave_id();
   if (w >= static_cast<int64_t>(nseg) * R) return;
   const int r = static_cast<int>(w / nseg);
@@ -402,52 +417,41 @@ __global__ __launch_bounds__(kBlock) void accumulate_kernel(const Segment* __res
     return;
   }
   int tail = 0;
+  // The unrolled groups check every access against the end, as in the fused
+  // mean kernel (paced loads, no remainder loop).
   if (BF16) {
     const uint16_t* st = static_cast<const uint16_t*>(steps[k]) + g.start;
     if (vec_ok && (g.flags & kSegVecStart) && (reinterpret_cast<uintptr_t>(acc) & 15) == 0 &&
         (reinterpret_cast<uintptr_t>(st) & 7) == 0) {
       const int n4 = len >> 2;
-      int i = lane;
-      for (; i + 64 * (U - 1) < n4; i += 64 * U) {
+      for (int i = lane; i < n4; i += 64 * U) {
         v2u b[U];
         v4f a[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          b[u] = ld2u(st + 4 * (i + 64 * u));
-          if (!FIRST) a[u] = ld4(acc + 4 * (i + 64 * u));
+          if (i + 64 * u < n4) {
+            b[u] = ld2x<kAccNT>(st + 4 * (i + 64 * u));
+            if (!FIRST) a[u] = ld4x<kAccNT>(acc + 4 * (i + 64 * u));
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          v4f s4;
-          s4.x = __uint_as_float(b[u].x << 16);
-          s4.y = __uint_as_float(b[u].x & 0xffff0000u);
-          s4.z = __uint_as_float(b[u].y << 16);
-          s4.w = __uint_as_float(b[u].y & 0xffff0000u);
-          if (!FIRST) {
-            s4.x = a[u].x + s4.x;
-            s4.y = a[u].y + s4.y;
-            s4.z = a[u].z + s4.z;
-            s4.w = a[u].w + s4.w;
+          if (i + 64 * u < n4) {
+            v4f s4;
+            s4.x = __uint_as_float(b[u].x << 16);
+            s4.y = __uint_as_float(b[u].x & 0xffff0000u);
+            s4.z = __uint_as_float(b[u].y << 16);
+            s4.w = __uint_as_float(b[u].y & 0xffff0000u);
+            if (!FIRST) {
+              s4.x = a[u].x + s4.x;
+              s4.y = a[u].y + s4.y;
+              s4.z = a[u].z + s4.z;
+              s4.w = a[u].w + s4.w;
+            }
+            st4x<kAccNT>(acc + 4 * (i + 64 * u), s4);
           }
-          st4(acc + 4 * (i + 64 * u), s4);
         }
-      }
-      for (; i < n4; i += 64) {
-        const v2u b = ld2u(st + 4 * i);
-        v4f s4;
-        s4.x = __uint_as_float(b.x << 16);
-        s4.y = __uint_as_float(b.x & 0xffff0000u);
-        s4.z = __uint_as_float(b.y << 16);
-        s4.w = __uint_as_float(b.y & 0xffff0000u);
-        if (!FIRST) {
-          const v4f a = ld4(acc + 4 * i);
-          s4.x = a.x + s4.x;
-          s4.y = a.y + s4.y;
-          s4.z = a.z + s4.z;
-          s4.w = a.w + s4.w;
-        }
-        st4(acc + 4 * i, s4);
       }
       tail = n4 * 4;
     }
@@ -460,16 +464,30 @@ __global__ __launch_bounds__(kBlock) void accumulate_kernel(const Segment* __res
     if (vec_ok && (g.flags & kSegVecStart) &&
         ((reinterpret_cast<uintptr_t>(acc) | reinterpret_cast<uintptr_t>(st)) & 15) == 0) {
       const int n4 = len >> 2;
-      for (int i = lane; i < n4; i += 64) {
-        v4f s4 = ld4(st + 4 * i);
-        if (!FIRST) {
-          const v4f a = ld4(acc + 4 * i);
-          s4.x = a.x + s4.x;
-          s4.y = a.y + s4.y;
-          s4.z = a.z + s4.z;
-          s4.w = a.w + s4.w;
+      for (int i = lane; i < n4; i += 64 * U) {
+        v4f b[U];
+        v4f a[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (i + 64 * u < n4) {
+            b[u] = ld4x<kAccNT>(st + 4 * (i + 64 * u));
+            if (!FIRST) a[u] = ld4x<kAccNT>(acc + 4 * (i + 64 * u));
+          }
         }
-        st4(acc + 4 * i, s4);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (i + 64 * u < n4) {
+            v4f s4 = b[u];
+            if (!FIRST) {
+              s4.x = a[u].x + s4.x;
+              s4.y = a[u].y + s4.y;
+              s4.z = a[u].z + s4.z;
+              s4.w = a[u].w + s4.w;
+            }
+            st4x<kAccNT>(acc + 4 * (i + 64 * u), s4);
+          }
+        }
       }
       tail = n4 * 4;
     }
