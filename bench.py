@@ -59,6 +59,9 @@ def parse():
                     help="the oracle repeats the sample's sync until this much CPU time")
     ap.add_argument("--no-time-launches", action="store_true",
                     help="do not record per-launch events (roofline becomes null)")
+    ap.add_argument("--hooks", choices=["each", "many"], default="each",
+                    help="each = one mark_ready call per hook from Python; many = the whole hook "
+                         "order in one mark_ready_many call (no binding overhead per hook)")
     return ap.parse_args()
 
 
@@ -225,6 +228,15 @@ def run_sync_bench(args, torch, D, WG, WC):
         red.bind(grads, compute_stream=compute, side_streams=sides, mode=mode, flags=flags)
     red.set_launch_blocks(args.launch_blocks or 0)
     order = w.ready_order()
+    if args.hooks == "many":
+        order_arr = list(order)
+
+        def one_sync():
+            red.mark_ready_many(order_arr)
+            red.finalize()
+    else:
+        def one_sync():
+            red.sync(order)
 
     # snapshot of the oracle's sample (first buckets), before any sync
     cpu = None
@@ -245,7 +257,7 @@ def run_sync_bench(args, torch, D, WG, WC):
         log(f"oracle sample: {nvars_sample} tensors, {sample_bytes / 1e6:.1f} MB per replica")
 
     for _ in range(args.warmup):
-        red.sync(order)
+        one_sync()
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps)")
 
@@ -258,9 +270,12 @@ def run_sync_bench(args, torch, D, WG, WC):
     read = 0                            # timed steps whose launch times were collected
     torch.cuda.synchronize()            # barrier (one process) + device sync
     t0 = time.perf_counter()
+    host_s = 0.0                        # host time inside the hooks and finalize
     evs[0].record(compute)
     for k in range(args.steps):
-        red.sync(order)
+        h0 = time.perf_counter()
+        one_sync()
+        host_s += time.perf_counter() - h0
         evs[k + 1].record(compute)
         # Collect launch times of steps that are about to leave the library's
         # ring, well behind the device, so the host never waits on recent work.
@@ -338,12 +353,14 @@ def run_sync_bench(args, torch, D, WG, WC):
         "data": "synthetic",
         "config": {"workload": w.name, "tensors": P, "params": sum(numels), "replicas": R,
                    "bucket_cap_bytes": w.cap_bytes, "buckets": B, "mode": args.mode,
-                   "side_streams": args.n_side, "alg_bytes_per_step": alg},
+                   "side_streams": args.n_side, "hooks": args.hooks, "alg_bytes_per_step": alg},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "hbm_copy_GBps": round(copy_gbps, 1),
         "ms_per_step_events": round(ev_ms, 4),
         "ms_per_sync_median": round(med_ms, 4),
         "ms_per_sync_p95": round(p95_ms, 4),
+        "host_ms_per_step": round(host_s * 1e3 / args.steps, 4),
+        "host_us_per_hook": round(host_s * 1e6 / (args.steps * P), 3),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "cpu_baseline_threads": cpu_threads,

@@ -599,8 +599,12 @@ class HipLauncher final : public Launcher {
     if (flags_ & 2) {
       ev_t0_.assign(B * kTimeRing, nullptr);
       ev_t1_.assign(B * kTimeRing, nullptr);
-      for (auto& e : ev_t0_) HIP_OK(hipEventCreate(&e), "hipEventCreate");
-      for (auto& e : ev_t1_) HIP_OK(hipEventCreate(&e), "hipEventCreate");
+      // Timing only: no system-scope fence when these complete, which would
+      // write back and invalidate caches between consecutive bucket kernels
+      // (measured: the timed sync lost 1.5 % with default events, 0.8 % without
+      // the fence).
+      for (auto& e : ev_t0_) HIP_OK(hipEventCreateWithFlags(&e, hipEventDisableSystemFence), "hipEventCreate");
+      for (auto& e : ev_t1_) HIP_OK(hipEventCreateWithFlags(&e, hipEventDisableSystemFence), "hipEventCreate");
     }
     return kOk;
   }
