@@ -438,7 +438,8 @@ def run_nosync_bench(args, torch, D, WG, WC):
         "accumulate_first_ms": round(sum(acc_first) / len(acc_first), 4),
         "accumulate_ms": round(avg_rest, 4), "sync_kernel_ms_last": round(sync_ms, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic_from_profiles("accumulate_kernel<bf16,add>", w.name),
                      "kernel": "accumulate_kernel<bf16,add>", "alg_bytes_per_launch": bytes_rest,
                      "avg_launch_us": round(avg_rest * 1e3, 2)},
         "cpu_baseline": None,
