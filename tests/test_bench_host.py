@@ -1,0 +1,65 @@
+"""CPU tests of the bench's host-side logic: the busy-time union of launch
+intervals, the traffic lookup keyed by the kernel sources' hash, and the
+refusal of more than one GPU."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+@pytest.mark.parametrize("starts,durs,want", [
+    ([], [], 0.0),
+    ([0.0], [2.0], 2.0),
+    ([0.0, 5.0], [2.0, 1.0], 3.0),            # disjoint
+    ([0.0, 1.0], [2.0, 2.0], 3.0),            # overlapping
+    ([0.0, 0.5], [3.0, 1.0], 3.0),            # nested
+    ([4.0, 0.0, 1.0], [1.0, 2.0, 2.0], 4.0),  # unsorted, touching
+])
+def test_union_length(starts, durs, want):
+    assert bench.union_length(starts, durs) == pytest.approx(want)
+
+
+def test_union_length_matches_brute_force():
+    import random
+    rng = random.Random(3)
+    for _ in range(200):
+        n = rng.randint(1, 12)
+        st = [rng.randint(0, 40) for _ in range(n)]
+        du = [rng.randint(0, 10) for _ in range(n)]
+        covered = set()
+        for s, d in zip(st, du):
+            covered.update(range(s, s + d))
+        assert bench.union_length(st, du) == pytest.approx(len(covered))
+
+
+def test_traffic_only_for_the_measured_sources(tmp_path, monkeypatch):
+    key = "fused_mean_kernel:some_workload"
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    entry = {"kernel_source_sha256_16": bench.kernel_source_hash(), "bytes_per_launch": 1234}
+    (prof / "traffic.json").write_text(json.dumps({key: entry}))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: entry["kernel_source_sha256_16"])
+    assert bench.traffic_from_profiles("fused_mean_kernel", "some_workload") == 1234
+    assert bench.traffic_from_profiles("fused_mean_kernel", "other_workload") is None
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)    # sources changed since
+    assert bench.traffic_from_profiles("fused_mean_kernel", "some_workload") is None
+
+
+def test_kernel_source_hash_covers_the_kernel_sources():
+    h = bench.kernel_source_hash()
+    assert len(h) == 16 and int(h, 16) >= 0
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2
+    assert "--gpus 1" in r.stderr
+    assert r.stdout == ""
