@@ -235,21 +235,82 @@ __global__ __launch_bounds__(kBlock) void fused_mean_kernel(const Segment* __res
   stamp_end(stamp);
 }
 
-// Any R (up to 64): runtime replica loop, same arithmetic order.
+// Any R (up to 64), runtime replica count, same arithmetic order: the
+// replicas are taken in chunks of kRtChunk whose loads all issue before the
+// chunk's adds (in replica order), two 1 KiB groups per lane in flight.
+constexpr int kRtChunk = 8;
+constexpr int kRtU = 2;
+
 __global__ __launch_bounds__(kBlock) void fused_mean_kernel_rt(const Segment* __restrict__ segs, int32_t nseg,
                                                                float* const* __restrict__ grads, int32_t P,
                                                                int32_t R, float scale, int32_t pow2,
-                                                               const uint8_t* __restrict__ used,
+                                                               int32_t vec_ok, const uint8_t* __restrict__ used,
                                                                int64_t* __restrict__ stamp) {
   stamp_begin(stamp);
+  const uint64_t all = R >= 64 ? ~0ull : ((1ull << R) - 1);
   // One wavefront per segment; with a capped grid (fewer workgroups than
   // segments / 4) each wavefront strides over the remaining segments.
   for (int s = blockIdx.x * kWavesPerBlock + wave_id(); s < nseg; s += gridDim.x * kWavesPerBlock) {
     const Segment g = segs[s];
     const int len = static_cast<int>(g.len);
+    const int lane = lane_id();
     const uint64_t mask = used_mask<uint64_t>(used, g.var, P, R);
     if (mask == 0) continue;
-    for (int j = lane_id(); j < len; j += 64) {
+    int tail = 0;
+    if (mask == all && vec_ok && (g.flags & kSegVecStart)) {
+      uintptr_t any = 0;                     // 16-byte alignment of every replica's pointer
+      for (int r = 0; r < R; ++r) any |= reinterpret_cast<uintptr_t>(grads[static_cast<int64_t>(r) * P + g.var]);
+      if (((any + static_cast<uintptr_t>(g.start) * 4) & 15) == 0) {
+        const int n4 = len >> 2;
+        for (int i = lane; i < n4; i += 64 * kRtU) {
+          v4f a[kRtU];
+          for (int r0 = 0; r0 < R; r0 += kRtChunk) {
+            v4f x[kRtU][kRtChunk];
+#pragma unroll
+            for (int u = 0; u < kRtU; ++u)
+#pragma unroll
+              for (int q = 0; q < kRtChunk; ++q)
+                if (r0 + q < R && i + 64 * u < n4)
+                  x[u][q] = ld4s(grads[static_cast<int64_t>(r0 + q) * P + g.var] + g.start + 4 * (i + 64 * u));
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < kRtU; ++u) {
+              if (i + 64 * u < n4) {
+#pragma unroll
+                for (int q = 0; q < kRtChunk; ++q) {
+                  if (r0 + q < R) {
+                    if (r0 + q == 0) {
+                      a[u] = x[u][q];
+                    } else {
+                      a[u].x = a[u].x + x[u][q].x;
+                      a[u].y = a[u].y + x[u][q].y;
+                      a[u].z = a[u].z + x[u][q].z;
+                      a[u].w = a[u].w + x[u][q].w;
+                    }
+                  }
+                }
+              }
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < kRtU; ++u) {
+            if (i + 64 * u < n4) {
+              v4f m;
+              m.x = finish_rt(a[u].x, R, scale, pow2 != 0);
+              m.y = finish_rt(a[u].y, R, scale, pow2 != 0);
+              m.z = finish_rt(a[u].z, R, scale, pow2 != 0);
+              m.w = finish_rt(a[u].w, R, scale, pow2 != 0);
+              for (int r = 0; r < R; ++r)
+                st4s(grads[static_cast<int64_t>(r) * P + g.var] + g.start + 4 * (i + 64 * u), m);
+            }
+          }
+        }
+        tail = n4 * 4;
+      }
+    }
+    // Scalar path: ragged tails, unaligned views, and variables some replicas
+    // did not use (their place in the order holds +0.0).
+    for (int j = tail + lane; j < len; j += 64) {
       float a = (mask & 1u) ? G(grads[g.var])[g.start + j] : 0.0f;
       for (int r = 1; r < R; ++r)
         a = a + (((mask >> r) & 1u) ? G(grads[static_cast<int64_t>(r) * P + g.var])[g.start + j] : 0.0f);
@@ -793,7 +854,7 @@ class HipLauncher final : public Launcher {
 #undef DDPB_FUSED_CASE
         default:
           hipExtLaunchKernelGGL(fused_mean_kernel_rt, grid, block, 0, s, t0, t1, 0, segs, nseg, table, tp, R_,
-                                scale_, pow2_ ? 1 : 0, used, stamp);
+                                scale_, pow2_ ? 1 : 0, vec_ok_, used, stamp);
       }
       HIP_OK(hipGetLastError(), "launch fused_mean_kernel");
       return kOk;
