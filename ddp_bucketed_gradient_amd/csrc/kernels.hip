@@ -324,6 +324,13 @@ __global__ __launch_bounds__(kBlock) void fused_mean_kernel_rt(const Segment* __
 // ---------------------------------------------------------------------------
 // staged path
 
+// Unroll of the staged kernels' copy loops (bound-checked groups, as in the
+// fused kernel). Gradients are streamed non-temporally; the flat buckets use
+// ordinary accesses so that a bucket packed by one kernel can still be in the
+// Infinity Cache when the mean kernel reads it.
+constexpr int kPackU = 8;
+constexpr int kCopybackU = 4;
+
 // R gradients -> R flat buckets (the narrowed views of [Li] "Gradient
 // Bucketing": view.copy_(grad)).
 __global__ __launch_bounds__(kBlock) void pack_kernel(const Segment* __restrict__ segs, int32_t nseg,
@@ -350,7 +357,16 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(const Segment* __restrict_
       int tail = 0;
       if (vec && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
         const int n4 = len >> 2;
-        for (int i = lane; i < n4; i += 64) st4(dst + 4 * i, ld4(src + 4 * i));
+        for (int i = lane; i < n4; i += 64 * kPackU) {
+          v4f x[kPackU];
+#pragma unroll
+          for (int u = 0; u < kPackU; ++u)
+            if (i + 64 * u < n4) x[u] = ld4s(src + 4 * (i + 64 * u));
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int u = 0; u < kPackU; ++u)
+            if (i + 64 * u < n4) st4(dst + 4 * (i + 64 * u), x[u]);
+        }
         tail = n4 * 4;
       }
       for (int j = tail + lane; j < len; j += 64) G(dst)[j] = G(src)[j];
@@ -421,9 +437,18 @@ __global__ __launch_bounds__(kBlock) void copyback_kernel(const Segment* __restr
     int tail = 0;
     if (vec) {
       const int n4 = len >> 2;
-      for (int i = lane; i < n4; i += 64) {
-        const v4f m = ld4(src + 4 * i);
-        for (int r = 0; r < R; ++r) st4(grads[static_cast<int64_t>(r) * P + g.var] + g.start + 4 * i, m);
+      for (int i = lane; i < n4; i += 64 * kCopybackU) {
+        v4f m[kCopybackU];
+#pragma unroll
+        for (int u = 0; u < kCopybackU; ++u)
+          if (i + 64 * u < n4) m[u] = ld4(src + 4 * (i + 64 * u));
+        __builtin_amdgcn_sched_barrier(0);
+        for (int r = 0; r < R; ++r) {
+          float* dst = grads[static_cast<int64_t>(r) * P + g.var] + g.start;
+#pragma unroll
+          for (int u = 0; u < kCopybackU; ++u)
+            if (i + 64 * u < n4) st4s(dst + 4 * (i + 64 * u), m[u]);
+        }
       }
       tail = n4 * 4;
     }
