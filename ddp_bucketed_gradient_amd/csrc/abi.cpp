@@ -286,6 +286,8 @@ int ddpb_get_launch_times(ddpb_t h, int32_t iterations_ago, float* start_ms, flo
   if (iterations_ago < 0 || iterations_ago >= ddpb::kTimeRing || iterations_ago >= fin)
     return fail(DDPB_E_INDEX, "get_launch_times: no such finalized iteration");
   const int64_t it = fin - 1 - iterations_ago;
+  if (it < h->red.timed_from())
+    return fail(DDPB_E_INDEX, "get_launch_times: that iteration ran before the current binding");
   const auto& log = h->red.log_of(it);
   *n = static_cast<int32_t>(log.size());
   const int32_t m = std::min<int32_t>(cap, *n);

@@ -133,6 +133,10 @@ int Reducer::bind(const BindArgs& args, std::string* err) {
     rc = launcher_->bind(plan_, args, err);
   }
   bound_ = (rc == kOk);
+  // The launch log and the timing history refer to the previous binding's
+  // buckets and events: start both afresh.
+  log_.clear();
+  timed_from_ = finalized_;
   return rc;
 }
 
@@ -300,6 +304,7 @@ int Reducer::rebuild_buckets(int64_t cap_bytes, std::string* err) {
   const std::vector<int32_t> order = last_order_;
   plan_ = make_plan(plan_.numel, plan_.elem_size, cap_bytes, plan_.R, &order);
   bound_ = false;                  // device tables and events follow the new plan at the next bind
+  log_.clear();
   begin_iteration();
   return kOk;
 }

@@ -164,6 +164,9 @@ class Reducer {
   int64_t finalized() const { return finalized_; }
   // Launches of finalized iteration `it` (only the last kTimeRing are kept).
   const std::vector<LaunchRecord>& log_of(int64_t it) const { return log_ring_[it % kTimeRing]; }
+  // First iteration launched with the current binding; launch times of
+  // earlier iterations belong to device resources that no longer exist.
+  int64_t timed_from() const { return timed_from_; }
   Launcher* launcher() { return launcher_.get(); }
 
  private:
@@ -189,6 +192,7 @@ class Reducer {
   int launch_ready(int32_t call, std::string* err);
   int mark_unused_ready(int32_t call, std::string* err);
   int64_t finalized_ = 0;          // iterations finalized so far
+  int64_t timed_from_ = 0;         // finalized_ at the last successful bind
   std::vector<LaunchRecord> log_ring_[kTimeRing];
 };
 

@@ -267,13 +267,15 @@ int ddpb_reset(ddpb_t h);
  * call that launched it, and, with DDPB_BIND_DEVICE_TIMESTAMPS, the device
  * clock (wall_clock64 ticks) at kernel start and end (else 0). Device values
  * are read with a blocking copy; synchronize the side streams first.
+ * A bind or a bucket rebuild empties the log.
  * Writes min(cap, count) entries and sets *n = count. */
 int ddpb_get_launch_log(ddpb_t h, int32_t* buckets, int32_t* trigger_call,
                         int64_t* dev_t0, int64_t* dev_t1, int32_t cap, int32_t* n);
 
 /* With DDPB_BIND_TIME_LAUNCHES: per launched bucket, in launch order, for the
  * finalized iteration `iterations_ago` back (0 = the last one; the last 64
- * iterations are kept, else DDPB_E_INDEX):
+ * iterations are kept, and only those run with the current binding, else
+ * DDPB_E_INDEX):
  *   ms[i]        duration from the start of the bucket's first kernel to the
  *                end of its last kernel (hipEvents attached to the dispatches)
  *   start_ms[i]  (may be NULL) start relative to the iteration's first launch,

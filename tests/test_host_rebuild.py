@@ -79,3 +79,21 @@ def test_rebuild_errors(host):
     with pytest.raises(D.DdpbError) as e:
         red.rebuild_buckets()                       # iteration in progress
     assert e.value.code == _abi.E_INCOMPLETE
+
+
+def test_rebind_starts_the_launch_history_afresh(host):
+    """After a rebuild and a new bind the old plan's launches are gone: the log
+    is empty and timing queries for iterations of the earlier binding fail
+    with an index error rather than reading the new binding's resources."""
+    numels = [5, 7, 3, 9]
+    red = D.Reducer([(n,) for n in numels], 2, 4 * 8, lib=host)
+    _bind(red)
+    red.sync([3, 2, 1, 0])
+    assert red.launch_log() != []
+    red.rebuild_buckets(0)
+    assert red.launch_log() == []
+    _bind(red)
+    assert red.launch_log() == []
+    with pytest.raises(D.DdpbError) as e:
+        red.launch_times_ms(0)
+    assert e.value.code == _abi.E_INDEX
