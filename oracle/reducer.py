@@ -120,7 +120,7 @@ class Reducer:
         reduction to be complete, then packs the parameters in their ready
         order with the same cap rule. Returns False when no finished iteration
         was recorded. In bucket-view mode the views are new (re-fetch them)."""
-        if self.failed or self.calls:
+        if self.failed or self.started:
             raise ReductionIncomplete("rebuild needs the prior iteration to have finished reducing")
         if self.last_ready_order is None:
             return False
@@ -143,6 +143,7 @@ class Reducer:
         self.ready = [False] * self.P
         self.next_bucket = 0
         self.calls = 0
+        self.started = False             # the iteration's first hook has run
         self.order_now = []
 
     def bind(self, grads: List[List[np.ndarray]]):
@@ -157,12 +158,12 @@ class Reducer:
         self.grads = grads
 
     def set_sync(self, enabled: bool):
-        if self.calls:
+        if self.started:
             raise RuntimeError("cannot toggle sync in the middle of an iteration")
         self.sync_enabled = bool(enabled)
 
     def ensure_prior_reduction_finished(self):
-        if self.failed or self.calls:
+        if self.failed or self.started:
             self.failed = True
             raise ReductionIncomplete(
                 "prior iteration did not finish reducing every bucket")
@@ -176,7 +177,7 @@ class Reducer:
         find_unused_parameters). Under no_sync the flags of successive calls
         are OR-ed together and serve the next synchronisation ([Li] "Gradient
         Accumulation (no_sync)"). Without any call every variable is used."""
-        if self.calls:
+        if self.started:
             raise RuntimeError("set_local_used must come before the iteration's hooks")
         u = np.asarray(used, dtype=bool).reshape(self.R, self.P)
         self.used_acc = u.copy() if self.used_acc is None else (self.used_acc | u)
@@ -218,7 +219,11 @@ class Reducer:
         if self.failed:
             raise ReductionIncomplete("prior iteration did not finish reducing every bucket")
         call = self.calls
-        if call == 0:
+        if not self.started:
+            # [C30] "Unused Parameter": unused variables are marked ready once
+            # per iteration, when its first hook runs (even if that hook then
+            # fails), never again within the iteration.
+            self.started = True
             self._mark_unused_ready(call)
         if self.ready[v]:
             raise DoubleReady(v)
@@ -260,10 +265,11 @@ class Reducer:
         self.launch_log.append((b, call))
 
     def finalize(self):
-        if not self.sync_enabled and self.calls == 0:
+        if not self.sync_enabled and not self.started:
             return
-        if self.calls == 0:
-            self._mark_unused_ready(0)   # no hook fired: only unused variables, if any
+        if not self.started:             # no hook fired: only unused variables, if any
+            self.started = True
+            self._mark_unused_ready(0)
         if self.next_bucket != self.B:
             self.failed = True
             raise ReductionIncomplete(

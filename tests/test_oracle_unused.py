@@ -138,3 +138,37 @@ def test_planted_unused_mistakes_are_caught(monkeypatch):
     monkeypatch.setattr(OR.Reducer, "set_local_used", and_used)
     with pytest.raises((AssertionError, OR.DoubleReady)):
         test_used_flags_accumulate_over_no_sync_steps()
+
+
+def _first_hook_names_an_unused_variable(cls):
+    """The iteration's first hook names a variable already marked ready as
+    unused (DoubleReady); the remaining hooks must still complete it, with the
+    unused marking applied once: cap 0, v2 -> bucket 0, v1 -> 1, v0 -> 2."""
+    red = cls([4, 4, 4], 2, 0)
+    g = [[WG.dyadic(50 + 3 * r + v, 4) for v in range(3)] for r in range(2)]
+    local = [[x.copy() for x in row] for row in g]
+    red.bind(g)
+    red.set_local_used([[True, False, True], [True, False, True]])
+    with pytest.raises(OR.DoubleReady):
+        red.mark_ready(1)
+    red.mark_ready(2)
+    red.mark_ready(0)
+    red.finalize()
+    assert red.launch_log == [(0, 0), (1, 0), (2, 1)]
+    for r in range(2):
+        assert np.array_equal(g[r][1], local[r][1])                  # unused: untouched
+        assert np.array_equal(g[r][0], OR.fixed_order_mean([local[0][0], local[1][0]]))
+
+
+def test_unused_marking_happens_once_even_after_a_failed_first_hook():
+    _first_hook_names_an_unused_variable(OR.Reducer)
+
+
+def test_planted_repeated_unused_marking_is_caught():
+    class Remarks(OR.Reducer):                   # keys the marking on the call count instead
+        def mark_ready(self, v):
+            if self.calls == 0:
+                self.started = False
+            return super().mark_ready(v)
+    with pytest.raises((AssertionError, OR.ReductionIncomplete)):
+        _first_hook_names_an_unused_variable(Remarks)
