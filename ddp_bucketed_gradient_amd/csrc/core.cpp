@@ -110,6 +110,7 @@ void Reducer::begin_iteration() {
   ready_.assign(plan_.P, 0);
   next_bucket_ = 0;
   calls_ = 0;
+  started_ = false;
   order_now_.clear();
 }
 
@@ -165,10 +166,16 @@ int Reducer::mark_ready(int32_t v, std::string* err) {
     *err = "the previous iteration left buckets unreduced; a new iteration cannot start before ddpb_reset";
     return kErrIncomplete;
   }
-  if (calls_ == 0) {
+  if (!started_) {
+    // [C30] "Unused Parameter": once per iteration, at its first hook (even if
+    // that hook then fails), the unused variables are marked ready.
+    started_ = true;
     log_.clear();
-    const int rc = mark_unused_ready(0, err);   // before the iteration's first hook
-    if (rc != kOk) return rc;
+    const int rc = mark_unused_ready(calls_, err);
+    if (rc != kOk) {
+      failed_ = true;
+      return rc;
+    }
   }
   if (ready_[v]) {
     *err = "mark_ready: variable marked ready twice in one iteration";
@@ -237,11 +244,15 @@ int Reducer::finalize(std::string* err) {
     *err = "finalize: reducer is not bound";
     return kErrState;
   }
-  if (!sync_ && calls_ == 0) return kOk;
-  if (!failed_ && calls_ == 0) {          // no hook fired: only unused variables, if any
+  if (!sync_ && !started_) return kOk;
+  if (!failed_ && !started_) {            // no hook fired: only unused variables, if any
+    started_ = true;
     log_.clear();
     const int rc = mark_unused_ready(0, err);
-    if (rc != kOk) return rc;
+    if (rc != kOk) {
+      failed_ = true;
+      return rc;
+    }
   }
   if (failed_ || next_bucket_ != plan_.B()) {
     failed_ = true;

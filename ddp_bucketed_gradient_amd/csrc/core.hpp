@@ -171,7 +171,7 @@ class Reducer {
 
  private:
   void begin_iteration();
-  bool iteration_open() const { return calls_ > 0; }
+  bool iteration_open() const { return started_; }
 
   Plan plan_;
   std::unique_ptr<Launcher> launcher_;
@@ -182,6 +182,7 @@ class Reducer {
   std::vector<uint8_t> ready_;     // per variable
   int32_t next_bucket_ = 0;
   int32_t calls_ = 0;              // mark_ready calls that counted, this iteration
+  bool started_ = false;           // the iteration's first hook has run (unused variables marked)
   std::vector<LaunchRecord> log_;
   std::vector<int32_t> order_now_;   // hook order of the current iteration
   std::vector<int32_t> last_order_;  // ... of the last finished iteration

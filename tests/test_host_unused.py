@@ -124,3 +124,38 @@ def test_flag_shape_checked(host):
     red, _ = _pair(host, [4, 4], 2, 0)
     with pytest.raises(ValueError):
         red.set_local_used([[True, True, True]])
+
+
+def test_failed_first_hook_marks_unused_once(host):
+    """First hook names a variable already marked ready as unused: DoubleReady,
+    then the remaining hooks complete the iteration as in the oracle (the
+    unused marking is not repeated)."""
+    red, orc = _pair(host, [4, 4, 4], 2, 0)
+    used = [[True, False, True], [True, False, True]]
+    red.set_local_used(used)
+    orc.set_local_used(used)
+    with pytest.raises(D.DdpbError) as e:
+        red.mark_ready(1)
+    assert e.value.code == _abi.E_DOUBLE_READY
+    with pytest.raises(OR.DoubleReady):
+        orc.mark_ready(1)
+    with pytest.raises(D.DdpbError) as e:         # the iteration has started
+        red.set_local_used(used)
+    assert e.value.code == _abi.E_STATE
+    for v in (2, 0):
+        red.mark_ready(v)
+        orc.mark_ready(v)
+    red.finalize()
+    orc.finalize()
+    assert red.launch_log() == orc.launch_log == [(0, 0), (1, 0), (2, 1)]
+
+
+def test_failed_first_hook_leaves_the_iteration_open(host):
+    red, _ = _pair(host, [4, 4], 2, 0)
+    red.set_local_used([[True, False], [True, False]])
+    with pytest.raises(D.DdpbError):
+        red.mark_ready(1)
+    with pytest.raises(D.DdpbError) as e:         # next forward: the iteration never finished
+        red.ensure_prior_reduction_finished()
+    assert e.value.code == _abi.E_INCOMPLETE
+    red.reset()
