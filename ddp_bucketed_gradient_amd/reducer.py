@@ -24,6 +24,12 @@ class Reducer:
         self.P = len(self.shapes)
         self.R = int(R)
         self.cap = int(bucket_cap_bytes)
+        self._numel = []
+        for s in self.shapes:
+            n = 1
+            for d in s:
+                n *= d
+            self._numel.append(n)
         self.h = self.lib.reducer_create(self.shapes, F32, self.cap, self.R)
         self._keep = []
 
@@ -55,9 +61,7 @@ class Reducer:
         for r in range(self.R):
             for v in range(self.P):
                 t = grads[r][v]
-                n = 1
-                for d in self.shapes[v]:
-                    n *= d
+                n = self._numel[v]
                 if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or t.numel() != n:
                     raise ValueError(f"grads[{r}][{v}] must be a contiguous fp32 CUDA tensor of {n} elements")
                 dev = t.device if dev is None else dev
@@ -106,9 +110,9 @@ class Reducer:
         """Re-plan the buckets from the last finished iteration's hook order.
         The reducer must be bound again afterwards (``bind`` or
         ``bind_bucket_views``; views change)."""
-        if bucket_cap_bytes is not None:
-            self.cap = int(bucket_cap_bytes)
-        self.lib.rebuild_buckets(self.h, self.cap)
+        cap = self.cap if bucket_cap_bytes is None else int(bucket_cap_bytes)
+        self.lib.rebuild_buckets(self.h, cap)
+        self.cap = cap
 
     def ready_order(self) -> List[int]:
         return self.lib.get_ready_order(self.h)
@@ -168,8 +172,10 @@ class Reducer:
                 if t is None:
                     ptrs.append(0)
                     continue
-                if t.dtype != dt or not t.is_contiguous():
-                    raise ValueError("step gradients must be contiguous and of one dtype")
+                if t.dtype != dt or not t.is_contiguous() or not t.is_cuda:
+                    raise ValueError("step gradients must be contiguous CUDA tensors of one dtype")
+                if t.numel() != self._numel[v]:
+                    raise ValueError(f"steps[{r}][{v}] has {t.numel()} elements, the variable {self._numel[v]}")
                 ptrs.append(t.data_ptr())
         self.lib.no_sync_accumulate(self.h, ptrs, code, first_step)
 

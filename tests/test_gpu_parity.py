@@ -492,3 +492,13 @@ def test_config5_overlap_parity(size):
     for v, bufs in pre.items():
         want = OR.fixed_order_mean(bufs)
         assert_bits_equal(grads[5][v].cpu().numpy(), want, f"v={v}")
+
+
+def test_wrong_size_step_is_refused_before_any_kernel():
+    red = D.Reducer([(4,), (6,)], 2, 0)
+    grads = alloc_grads([4, 6], 2)
+    red.bind(grads)
+    bad = [[torch.zeros(4, device="cuda"), torch.zeros(5, device="cuda")] for _ in range(2)]
+    with pytest.raises(ValueError):
+        red.no_sync_accumulate(bad, True)
+    red.close()

@@ -254,3 +254,25 @@ def test_empty_model(host):
     assert red.num_buckets == 0
     red.bind_ptrs([], side_streams=[0])
     red.finalize()
+
+
+def test_binding_checks_step_tensors_before_the_library_sees_them(host):
+    """A step tensor of the wrong size, dtype or device never reaches the
+    kernels: the binding raises first (CPU tensors stand in for the wrong
+    device here)."""
+    import torch
+    red = D.Reducer([(4,), (6,)], 2, 0, lib=host)
+    _bind_fake(red)
+    ok = [[torch.zeros(4), torch.zeros(6)] for _ in range(2)]
+    with pytest.raises(ValueError):
+        red.no_sync_accumulate(ok, True)                      # not CUDA tensors
+    with pytest.raises(ValueError):
+        red.no_sync_accumulate([[torch.zeros(4, dtype=torch.float16), None]] * 2, True)
+
+
+def test_failed_rebuild_keeps_the_cap(host):
+    red = D.Reducer([(4,), (6,)], 2, 8, lib=host)
+    _bind_fake(red)
+    with pytest.raises(D.DdpbError):
+        red.rebuild_buckets(0)                                # no finished iteration yet
+    assert red.cap == 8
