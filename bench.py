@@ -67,9 +67,10 @@ def parse():
 
 def kernel_source_hash() -> str:
     """sha256 prefix of the sources that decide what the kernels read and
-    write (kernels, segment planner)."""
+    write: the kernels and their launcher, the segment planner and the
+    descriptor layout they share (not the readiness state machine)."""
     h = hashlib.sha256()
-    for name in ("kernels.hip", "core.hpp", "core.cpp"):
+    for name in ("kernels.hip", "core.hpp", "plan.cpp"):
         with open(os.path.join(ROOT, "ddp_bucketed_gradient_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

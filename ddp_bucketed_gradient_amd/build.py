@@ -26,7 +26,7 @@ HIP_LIB = os.path.join(LIBDIR, "libddpb.so")
 HOST_LIB = os.path.join(LIBDIR, "libddpb_hostonly.so")
 ARCH = "gfx950"
 
-HOST_SOURCES = ["core.cpp", "abi.cpp"]
+HOST_SOURCES = ["plan.cpp", "core.cpp", "abi.cpp"]
 
 # -ffp-contract=off: no fused multiply-add may change the rounding of the mean.
 # packed-fp32-ops disabled: the float4 adds stay scalar v_add_f32.

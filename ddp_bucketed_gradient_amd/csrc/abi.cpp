@@ -1,5 +1,5 @@
 // abi.cpp -- the extern "C" surface declared in include/ddpb.h. Argument
-// checking and marshalling only; the work happens in core.cpp and the
+// checking and marshalling only; the work happens in plan.cpp, core.cpp and the
 // launcher.
 #include <algorithm>
 #include <cstring>

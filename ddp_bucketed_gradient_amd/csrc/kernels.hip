@@ -10,7 +10,7 @@
 // once with 128-bit accesses and does a handful of adds per element.
 //
 // Work decomposition: the host cuts every bucket member into segments of at
-// most kSegElems (8192) elements (core.cpp). One wavefront owns one segment; a workgroup
+// most kSegElems (8192) elements (plan.cpp). One wavefront owns one segment; a workgroup
 // of 256 threads owns four consecutive segments. Each lane moves v4fs at
 // lane stride, so one instruction covers 1 KiB of contiguous memory per
 // replica, and it issues all R (x unroll) loads before the first add to keep
