@@ -16,7 +16,8 @@ by the wall-clock time per step.
 Other workloads (not the default line): ``--config 2`` (ResNet-50 shapes),
 ``--config 4`` (no_sync: BERT-base shapes, R=16, 8 bf16 micro-steps, then one
 sync), ``--config 5`` (overlap with a bf16 MLP backward), ``--cap-mib``,
-``--mode staged``, ``--n-side``.
+``--mode staged|view``, ``--n-side``, ``--graph`` (replays of one captured
+sync), ``--hooks many`` (all hooks in one call).
 """
 from __future__ import annotations
 
@@ -59,6 +60,9 @@ def parse():
                     help="the oracle repeats the sample's sync until this much CPU time")
     ap.add_argument("--no-time-launches", action="store_true",
                     help="do not record per-launch events (roofline becomes null)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one whole sync into a HIP graph after warm-up and time its replays "
+                         "(no per-launch events: roofline becomes null)")
     ap.add_argument("--hooks", choices=["each", "many"], default="each",
                     help="each = one mark_ready call per hook from Python; many = the whole hook "
                          "order in one mark_ready_many call (no binding overhead per hook)")
@@ -208,7 +212,7 @@ def run_sync_bench(args, torch, D, WG, WC):
 
     red = D.Reducer([p.shape for p in params], R, w.cap_bytes)
     B = red.num_buckets
-    flags = 0 if args.no_time_launches else D.BIND_TIME_LAUNCHES
+    flags = 0 if (args.no_time_launches or args.graph) else D.BIND_TIME_LAUNCHES
     # The compute stream and the side streams are consecutive streams of
     # torch's pool, so the HIP runtime places them on distinct hardware queues
     # (it hands out its 4 queues round-robin); the legacy null stream stays idle.
@@ -261,6 +265,17 @@ def run_sync_bench(args, torch, D, WG, WC):
         one_sync()
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps)")
+    run_step = one_sync
+    if args.graph:                      # replays repeat the captured device work only
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=compute):
+            one_sync()
+        torch.cuda.synchronize()
+        run_step = graph.replay
+        for _ in range(args.warmup):
+            run_step()
+        torch.cuda.synchronize()
+        log("captured one sync into a graph")
 
     # one event on the compute stream before each sync and after the last: the
     # interval between consecutive events is one sync (from the previous join
@@ -275,7 +290,7 @@ def run_sync_bench(args, torch, D, WG, WC):
     evs[0].record(compute)
     for k in range(args.steps):
         h0 = time.perf_counter()
-        one_sync()
+        run_step()
         host_s += time.perf_counter() - h0
         evs[k + 1].record(compute)
         # Collect launch times of steps that are about to leave the library's
@@ -354,7 +369,8 @@ def run_sync_bench(args, torch, D, WG, WC):
         "data": "synthetic",
         "config": {"workload": w.name, "tensors": P, "params": sum(numels), "replicas": R,
                    "bucket_cap_bytes": w.cap_bytes, "buckets": B, "mode": args.mode,
-                   "side_streams": args.n_side, "hooks": args.hooks, "alg_bytes_per_step": alg},
+                   "side_streams": args.n_side, "hooks": args.hooks, "graph": args.graph,
+                   "alg_bytes_per_step": alg},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "hbm_copy_GBps": round(copy_gbps, 1),
         "ms_per_step_events": round(ev_ms, 4),

@@ -604,6 +604,17 @@ __global__ __launch_bounds__(kBlock) void zero_unused_kernel(const Segment* __re
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// Whether work enqueued on `s` now is being recorded into a graph rather than
+// run. A replayed graph repeats the recorded device work only, so anything
+// that reads host memory at run time (a pinned-staging upload) or whose
+// result the host reads back (launch-timing events) must not be recorded.
+int capturing(hipStream_t s, bool* yes, std::string* err) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  HIP_OK(hipStreamIsCapturing(s, &st), "hipStreamIsCapturing");
+  *yes = (st != hipStreamCaptureStatusNone);
+  return kOk;
+}
+
 class HipLauncher final : public Launcher {
  public:
   ~HipLauncher() override { release(); }
@@ -697,6 +708,14 @@ class HipLauncher final : public Launcher {
 
   int launch(int32_t first, int32_t last, int64_t iteration, std::string* err) override {
     const size_t ring = static_cast<size_t>(iteration % kTimeRing) * plan_->B();
+    if (flags_ & 2) {
+      bool cap = false;
+      if (const int rc = capturing(compute_, &cap, err); rc != kOk) return rc;
+      if (cap) {
+        *err = "launch timing cannot be captured into a graph; bind without DDPB_BIND_TIME_LAUNCHES";
+        return kErrState;
+      }
+    }
     HIP_OK(hipEventRecord(ev_ready_[first], compute_), "hipEventRecord(ready)");
     uint32_t waited = 0;
     for (int32_t b = first; b <= last; ++b) {
@@ -730,6 +749,12 @@ class HipLauncher final : public Launcher {
   int accumulate(void* const* step_ptrs, int32_t step_dtype, bool first, std::string* err) override {
     const size_t nptr = static_cast<size_t>(R_) * P_;
     if (plan_->segs.empty()) return kOk;
+    bool cap = false;
+    if (const int rc = capturing(compute_, &cap, err); rc != kOk) return rc;
+    if (cap) {                     // the step table comes from host staging that later calls reuse
+      *err = "no_sync_accumulate cannot be captured into a graph";
+      return kErrState;
+    }
     const int vec = vec_ok_;       // alignment is checked per segment in the kernel
     // Step pointer tables go through a small ring of device slots; a table
     // seen recently is reused without another upload.
@@ -815,6 +840,12 @@ class HipLauncher final : public Launcher {
     }
     const size_t n = static_cast<size_t>(R_) * P_;
     if (n == 0) return kOk;
+    bool cap = false;
+    if (const int rc = capturing(compute_, &cap, err); rc != kOk) return rc;
+    if (cap) {                     // the flags come from host staging that later calls reuse
+      *err = "an iteration with used flags (ddpb_set_local_used) cannot be captured into a graph";
+      return kErrState;
+    }
     // The staging buffer may still feed the previous upload.
     if (used_recorded_) HIP_OK(hipEventSynchronize(ev_used_), "hipEventSynchronize(used)");
     std::memcpy(h_used_, used, n);

@@ -218,6 +218,18 @@ int ddpb_mark_ready_many(ddpb_t h, const int32_t* vs, int32_t n);
  * variable was marked. */
 int ddpb_finalize(ddpb_t h);
 
+/* Graph capture. A whole synchronisation (the ddpb_mark_ready calls and
+ * ddpb_finalize) may be recorded into a HIP graph by capturing the bound
+ * compute stream: the library's event record on the compute stream forks the
+ * side streams into the capture and finalize's join brings them back, so the
+ * graph holds every bucket kernel with its ordering. Replaying the graph
+ * repeats the device work only; the host state machine advanced once, at
+ * capture. Refused during capture (DDPB_E_STATE, nothing recorded):
+ * ddpb_no_sync_accumulate and an iteration with ddpb_set_local_used flags
+ * (both upload tables from host staging that later calls reuse), and any
+ * launch of a binding made with DDPB_BIND_TIME_LAUNCHES. A refusal inside
+ * ddpb_mark_ready latches DDPB_E_INCOMPLETE like any failed launch. */
+
 /* The no_sync() switch ([Li] "Gradient Accumulation (no_sync)"; [TP] "Gradient
  * sync you can turn off"): enabled = 0 makes ddpb_mark_ready a no-op.
  * DDPB_E_STATE if an iteration is in progress. */
