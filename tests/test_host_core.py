@@ -276,3 +276,9 @@ def test_failed_rebuild_keeps_the_cap(host):
     with pytest.raises(D.DdpbError):
         red.rebuild_buckets(0)                                # no finished iteration yet
     assert red.cap == 8
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """No fallback: without the built library the binding raises."""
+    with pytest.raises(ImportError, match="no fallback"):
+        D.Lib(str(tmp_path / "libddpb.so"))
