@@ -267,6 +267,8 @@ class Reducer:
     def finalize(self):
         if not self.sync_enabled and not self.started:
             return
+        if self.failed:                  # latched until reset, like the hooks
+            raise ReductionIncomplete("prior iteration did not finish reducing every bucket")
         if not self.started:             # no hook fired: only unused variables, if any
             self.started = True
             self._mark_unused_ready(0)

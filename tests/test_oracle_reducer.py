@@ -358,3 +358,21 @@ def test_planted_copyback_mistake_is_caught(monkeypatch):
     monkeypatch.setattr(OR.Reducer, "_launch", only_rank0)
     with pytest.raises(AssertionError):
         test_every_replica_gets_exact_rounded_mean_on_dyadic_inputs(3)
+
+
+def test_latched_failure_refuses_finalize_until_reset():
+    """[TP] "When a parameter never receives a gradient": an iteration left
+    open is reported at the next forward; the reading taken here latches that
+    failure, so the open iteration cannot be finalized afterwards either, and a
+    reset restores normal operation."""
+    red = OR.Reducer([4], 2, 0)
+    g = [[np.ones(4, np.float32)], [np.ones(4, np.float32)]]
+    red.bind(g)
+    red.mark_ready(0)                        # every bucket launched, finalize not yet called
+    with pytest.raises(OR.ReductionIncomplete):
+        red.ensure_prior_reduction_finished()
+    with pytest.raises(OR.ReductionIncomplete):
+        red.finalize()
+    red.reset()
+    red.sync()
+    assert len(red.launch_log) == 2
