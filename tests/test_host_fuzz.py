@@ -1,0 +1,120 @@
+"""Differential fuzz of the native readiness state machine (host-only build)
+against the oracle: random sequences of hooks (repeated and out-of-range ones
+included), finalize, no_sync toggles, used flags, ready-order rebuilds, resets
+and next-forward checks. After every operation both sides must have succeeded
+or failed with the same kind of error, and every finished iteration must have
+launched the same buckets at the same hook calls."""
+import os
+
+import numpy as np
+import pytest
+
+import ddp_bucketed_gradient_amd as D
+from ddp_bucketed_gradient_amd import _abi
+from oracle import reducer as OR
+from workloads import gen as WG
+
+
+@pytest.fixture(scope="module")
+def host():
+    if not os.path.exists(D.HOSTONLY_LIB):
+        from ddp_bucketed_gradient_amd import build
+        build.build_hostonly()
+    return D.Lib(D.HOSTONLY_LIB)
+
+
+def _kind_native(e):
+    return {_abi.E_INDEX: "index", _abi.E_DOUBLE_READY: "double", _abi.E_INCOMPLETE: "incomplete",
+            _abi.E_STATE: "state"}.get(e.code, f"other {e.code}")
+
+
+def _kind_oracle(e):
+    if isinstance(e, OR.DoubleReady):
+        return "double"
+    if isinstance(e, OR.ReductionIncomplete):
+        return "incomplete"
+    if isinstance(e, IndexError):
+        return "index"
+    if isinstance(e, RuntimeError):
+        return "state"
+    return f"other {type(e).__name__}"
+
+
+def _both(fn_native, fn_oracle):
+    kn = ko = None
+    rn = ro = None
+    try:
+        rn = fn_native()
+    except D.DdpbError as e:
+        kn = _kind_native(e)
+    try:
+        ro = fn_oracle()
+    except (OR.DoubleReady, OR.ReductionIncomplete, IndexError, RuntimeError) as e:
+        ko = _kind_oracle(e)
+    return kn, ko, rn, ro
+
+
+def _run(host, seed):
+    rng = np.random.default_rng(seed)
+    P = int(rng.integers(1, 9))
+    R = int(rng.integers(1, 4))
+    numels = WG.random_numels(seed, P, 1, 40)
+    cap = int(rng.integers(0, 4 * sum(numels) + 1))
+    red = D.Reducer([(n,) for n in numels], R, cap, lib=host)
+
+    def bind():
+        red.bind_ptrs([0x1000 + 64 * i for i in range(R * P)], side_streams=[0])
+
+    bind()
+    orc = OR.Reducer(numels, R, cap)
+    orc.bind([[np.zeros(n, np.float32) for n in numels] for _ in range(R)])
+    log_start = 0
+    trace = []
+    for step in range(60):
+        op = rng.choice(["hook", "hook", "hook", "hook", "finalize", "used", "sync", "rebuild", "reset",
+                         "forward"], p=[.15, .15, .15, .15, .12, .08, .06, .05, .04, .05])
+        if op == "hook":
+            v = int(rng.integers(-1, P + 1))
+            kn, ko, _, _ = _both(lambda: red.mark_ready(v), lambda: orc.mark_ready(v))
+        elif op == "finalize":
+            kn, ko, _, _ = _both(red.finalize, orc.finalize)
+            if kn is None and ko is None and orc.sync_enabled:
+                assert red.launch_log() == orc.launch_log[log_start:], (seed, step, trace)
+            log_start = len(orc.launch_log)
+        elif op == "used":
+            used = rng.random((R, P)) < 0.7
+            kn, ko, _, _ = _both(lambda: red.set_local_used(used), lambda: orc.set_local_used(used))
+        elif op == "sync":
+            en = bool(rng.integers(0, 2))
+            kn, ko, _, _ = _both(lambda: red.set_sync(en), lambda: orc.set_sync(en))
+        elif op == "rebuild":
+            c = int(rng.integers(0, 4 * sum(numels) + 1))
+
+            def native_rebuild():
+                red.rebuild_buckets(c)
+                return True
+
+            def oracle_rebuild():
+                ok = orc.rebuild_buckets(c)
+                if not ok:
+                    raise RuntimeError("no recorded order")      # the native call reports E_STATE
+                return True
+
+            kn, ko, rn, ro = _both(native_rebuild, oracle_rebuild)
+            if kn is None and ko is None:
+                assert red.buckets() == orc.buckets, (seed, step)
+                bind()
+                log_start = len(orc.launch_log)
+        elif op == "reset":
+            kn, ko, _, _ = _both(red.reset, orc.reset)
+            log_start = len(orc.launch_log)
+        else:
+            kn, ko, _, _ = _both(red.ensure_prior_reduction_finished, orc.ensure_prior_reduction_finished)
+        trace.append((op, kn, ko))
+        assert kn == ko, (seed, step, trace)
+
+
+@pytest.mark.parametrize("block", range(10))
+def test_state_machine_agrees_with_the_oracle(host, block):
+    for seed in range(block * 30, block * 30 + 30):
+        _run(host, seed)
