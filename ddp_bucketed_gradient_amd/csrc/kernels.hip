@@ -171,10 +171,38 @@ __global__ __launch_bounds__(kBlock) void fused_mean_kernel(const Segment* __res
     const int lane = lane_id();
     const uint32_t mask = used_mask<uint32_t>(used, g.var, P, R);
     if (mask == 0) continue;                 // no replica used it: leave every gradient untouched
+    uintptr_t any = 0;                       // 16-byte alignment of every replica's pointer
+#pragma unroll
+    for (int r = 0; r < R; ++r) any |= reinterpret_cast<uintptr_t>(p[r]);
     if (mask != kAll) {
       // Some replicas did not use this variable: their bucket slice is zero,
-      // so they add +0.0 in their place of the fixed order.
-      for (int j = lane; j < len; j += 64) {
+      // so they add +0.0 in their place of the fixed order (their gradients
+      // are not read). The mask is the same for the whole wavefront.
+      constexpr int UM = 2;
+      int mtail = 0;
+      if (vec_ok && (g.flags & kSegVecStart) && (any & 15) == 0) {
+        const int n4 = len >> 2;
+        const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int i = lane; i < n4; i += 64 * UM) {
+          v4f x[UM][R];
+#pragma unroll
+          for (int u = 0; u < UM; ++u)
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+              if (i + 64 * u < n4) x[u][r] = ((mask >> r) & 1u) ? ld4s(p[r] + 4 * (i + 64 * u)) : zero;
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int u = 0; u < UM; ++u) {
+            if (i + 64 * u < n4) {
+              const v4f m = mean4<R>(x[u], scale);
+#pragma unroll
+              for (int r = 0; r < R; ++r) st4s(p[r] + 4 * (i + 64 * u), m);
+            }
+          }
+        }
+        mtail = n4 * 4;
+      }
+      for (int j = mtail + lane; j < len; j += 64) {
         float x[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) x[r] = ((mask >> r) & 1u) ? G(p[r])[j] : 0.0f;
@@ -187,9 +215,6 @@ __global__ __launch_bounds__(kBlock) void fused_mean_kernel(const Segment* __res
       }
       continue;
     }
-    uintptr_t any = 0;                       // 16-byte alignment of every replica's pointer
-#pragma unroll
-    for (int r = 0; r < R; ++r) any |= reinterpret_cast<uintptr_t>(p[r]);
     int tail = 0;
     if (vec_ok && (g.flags & kSegVecStart) && (any & 15) == 0) {
       const int n4 = len >> 2;
