@@ -272,7 +272,6 @@ __global__ __launch_bounds__(kBlock) void fused_mean_kernel_rt(const Segment* __
                                                                int32_t vec_ok, const uint8_t* __restrict__ used,
                                                                int64_t* __restrict__ stamp) {
   stamp_begin(stamp);
-  const uint64_t all = R >= 64 ? ~0ull : ((1ull << R) - 1);
   // One wavefront per segment; with a capped grid (fewer workgroups than
   // segments / 4) each wavefront strides over the remaining segments.
   for (int s = blockIdx.x * kWavesPerBlock + wave_id(); s < nseg; s += gridDim.x * kWavesPerBlock) {
@@ -282,7 +281,7 @@ __global__ __launch_bounds__(kBlock) void fused_mean_kernel_rt(const Segment* __
     const uint64_t mask = used_mask<uint64_t>(used, g.var, P, R);
     if (mask == 0) continue;
     int tail = 0;
-    if (mask == all && vec_ok && (g.flags & kSegVecStart)) {
+    if (vec_ok && (g.flags & kSegVecStart)) {
       uintptr_t any = 0;                     // 16-byte alignment of every replica's pointer
       for (int r = 0; r < R; ++r) any |= reinterpret_cast<uintptr_t>(grads[static_cast<int64_t>(r) * P + g.var]);
       if (((any + static_cast<uintptr_t>(g.start) * 4) & 15) == 0) {
@@ -296,7 +295,9 @@ __global__ __launch_bounds__(kBlock) void fused_mean_kernel_rt(const Segment* __
 #pragma unroll
               for (int q = 0; q < kRtChunk; ++q)
                 if (r0 + q < R && i + 64 * u < n4)
-                  x[u][q] = ld4s(grads[static_cast<int64_t>(r0 + q) * P + g.var] + g.start + 4 * (i + 64 * u));
+                  x[u][q] = ((mask >> (r0 + q)) & 1u)   // +0.0 for a replica that did not use it
+                                ? ld4s(grads[static_cast<int64_t>(r0 + q) * P + g.var] + g.start + 4 * (i + 64 * u))
+                                : v4f{0.0f, 0.0f, 0.0f, 0.0f};
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int u = 0; u < kRtU; ++u) {
@@ -333,8 +334,8 @@ __global__ __launch_bounds__(kBlock) void fused_mean_kernel_rt(const Segment* __
         tail = n4 * 4;
       }
     }
-    // Scalar path: ragged tails, unaligned views, and variables some replicas
-    // did not use (their place in the order holds +0.0).
+    // Scalar path: ragged tails and unaligned views (a replica that did not
+    // use the variable holds +0.0 in its place of the order).
     for (int j = tail + lane; j < len; j += 64) {
       float a = (mask & 1u) ? G(grads[g.var])[g.start + j] : 0.0f;
       for (int r = 1; r < R; ++r)
