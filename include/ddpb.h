@@ -129,8 +129,11 @@ int ddpb_workspace_bytes(ddpb_t h, int32_t mode, int64_t* bytes);
  *   workspace      device buffer of >= ddpb_workspace_bytes(mode) bytes (may
  *                  be NULL when that is 0), 256-byte aligned.
  *   compute_stream stream on which gradients are produced (hipStream_t).
- *   side_streams   n_side >= 1 streams for the reduction kernels; bucket b
- *                  runs on side_streams[b % n_side].
+ *   side_streams   n_side (1..16) streams for the reduction kernels; bucket b
+ *                  runs on side_streams[b % n_side]. Keep them on hardware
+ *                  queues of their own (with 4 queues per process, the
+ *                  compute stream and two side streams created one after the
+ *                  other are placed apart).
  *   mode, flags    DDPB_MODE_*, DDPB_BIND_*.
  * Synchronizes the compute stream once to upload the tables. Not allowed
  * while an iteration is in progress. */
@@ -190,8 +193,9 @@ int ddpb_set_launch_blocks(ddpb_t h, int32_t max_blocks);
 
 /* The check a wrapper's forward makes before a new iteration: returns
  * DDPB_E_INCOMPLETE (and latches that state until ddpb_reset) when the
- * previous iteration marked variables ready but did not finish reducing
- * every bucket ([TP] "When a parameter never receives a gradient"). */
+ * previous iteration was left open -- its first hook ran but ddpb_finalize
+ * did not complete it ([TP] "When a parameter never receives a gradient").
+ * While latched, ddpb_mark_ready and ddpb_finalize fail the same way. */
 int ddpb_ensure_prior_reduction_finished(ddpb_t h);
 
 /* Hook for variable v: its gradient is final on every replica, ordered on the
