@@ -581,7 +581,7 @@ def run_overlap_bench(args, torch, D, WG, WC):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported: this build emulates the R data-parallel "
+        print(f"bench.py: --gpus {args.gpus} is not supported: the library emulates the R data-parallel "
               "replicas inside one GPU's HBM and has no collective between GPUs; run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
