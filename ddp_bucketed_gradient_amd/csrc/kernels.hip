@@ -10,15 +10,18 @@
 // once with 128-bit accesses and does a handful of adds per element.
 //
 // Work decomposition: the host cuts every bucket member into segments of at
-// most kSegElems (8192) elements (plan.cpp). One wavefront owns one segment; a workgroup
-// of 256 threads owns four consecutive segments. Each lane moves v4fs at
-// lane stride, so one instruction covers 1 KiB of contiguous memory per
-// replica, and it issues all R (x unroll) loads before the first add to keep
-// enough bytes in flight.
+// most kSegElems (8192) elements (plan.cpp). One wavefront owns one segment;
+// a workgroup of 256 threads owns four consecutive segments. Each lane moves
+// v4fs at lane stride, so one instruction covers 1 KiB of contiguous memory
+// per replica. An unrolled group issues all of its R x U loads before the
+// first add, to keep enough bytes in flight, each under its own bound check
+// so that they leave one at a time (measured faster than back to back).
 //
 // Kernels
 //   fused_mean_kernel   gather (pack), R-way mean and copy-back in one pass:
 //                       reads R*S_b and writes R*S_b bytes per bucket.
+//   fused_mean_kernel_rt  the same for a replica count known at run time
+//                       (above 16), replicas in chunks of 8.
 //   pack_kernel         staged step 1: R gradients -> R flat buckets.
 //   mean_kernel         staged step 2: R flat buckets -> averaged bucket,
 //                       grid-stride over contiguous v4fs.
@@ -82,7 +85,6 @@ __device__ __forceinline__ void st4s(float* p, v4f v) { __builtin_nontemporal_st
 
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(1))) v2u gv2u;
-__device__ __forceinline__ v2u ld2u(const uint16_t* p) { return *(const gv2u*)p; }
 
 template <int R>
 __device__ __forceinline__ float finish(float acc, float scale) {
@@ -506,7 +508,7 @@ template <bool NT>
 __device__ __forceinline__ void st4x(float* p, v4f v) { if constexpr (NT) st4s(p, v); else st4(p, v); }
 template <bool NT>
 __device__ __forceinline__ v2u ld2x(const uint16_t* p) {
-  if constexpr (NT) return __builtin_nontemporal_load((const gv2u*)p); else return ld2u(p);
+  if constexpr (NT) return __builtin_nontemporal_load((const gv2u*)p); else return *(const gv2u*)p;
 }
 
 template <bool BF16, bool FIRST>
