@@ -63,6 +63,9 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="capture one whole sync into a HIP graph after warm-up and time its replays "
                          "(no per-launch events: roofline becomes null)")
+    ap.add_argument("--unused-frac", type=float, default=0.0,
+                    help="fraction of (replica, variable) pairs marked unused before every sync "
+                         "(seeded; at least one replica uses each variable)")
     ap.add_argument("--hooks", choices=["each", "many"], default="each",
                     help="each = one mark_ready call per hook from Python; many = the whole hook "
                          "order in one mark_ready_many call (no binding overhead per hook)")
@@ -233,14 +236,25 @@ def run_sync_bench(args, torch, D, WG, WC):
         red.bind(grads, compute_stream=compute, side_streams=sides, mode=mode, flags=flags)
     red.set_launch_blocks(args.launch_blocks or 0)
     order = w.ready_order()
+    used = None
+    if args.unused_frac > 0:
+        import numpy as np
+        rng = np.random.default_rng(7)
+        used = rng.random((R, P)) >= args.unused_frac
+        used[rng.integers(0, R, size=P), np.arange(P)] = True     # every variable used somewhere
+        log(f"unused pairs: {int((~used).sum())} of {R * P}")
     if args.hooks == "many":
         order_arr = list(order)
 
         def one_sync():
+            if used is not None:
+                red.set_local_used(used)
             red.mark_ready_many(order_arr)
             red.finalize()
     else:
         def one_sync():
+            if used is not None:
+                red.set_local_used(used)
             red.sync(order)
 
     # snapshot of the oracle's sample (first buckets), before any sync
@@ -249,7 +263,9 @@ def run_sync_bench(args, torch, D, WG, WC):
     host_in = None
     nvars_sample = 0
     sample_bytes = 0
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.unused_frac > 0:
+        log("no CPU baseline with --unused-frac (the oracle leg times the plain sync)")
+    elif not args.no_cpu_baseline:
         budget = args.cpu_sample_gb * 1e9 / (2 * R)
         for b in range(B):
             vars_b, nb = red.lib.get_bucket(red.h, b)
@@ -314,6 +330,11 @@ def run_sync_bench(args, torch, D, WG, WC):
     log(f"timed {args.steps} steps: {wall_ms:.3f} ms/step wall, {ev_ms:.3f} ms/step events")
 
     alg = 2 * R * S
+    if used is not None:
+        # unused pairs are not read; every variable is used by some replica,
+        # so the mean is still written to every replica
+        import numpy as np
+        alg = 4 * int((used * np.asarray(numels, dtype=np.int64)[None, :]).sum()) + R * S
     value = alg / (wall_ms * 1e-3) / 1e9
     kernel = {"fused": "fused_mean_kernel", "view": "fused_mean_kernel(bucket view)",
               "staged": "pack+mean+copyback"}[args.mode]
@@ -370,6 +391,7 @@ def run_sync_bench(args, torch, D, WG, WC):
         "config": {"workload": w.name, "tensors": P, "params": sum(numels), "replicas": R,
                    "bucket_cap_bytes": w.cap_bytes, "buckets": B, "mode": args.mode,
                    "side_streams": args.n_side, "hooks": args.hooks, "graph": args.graph,
+                   "unused_frac": args.unused_frac,
                    "alg_bytes_per_step": alg},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "hbm_copy_GBps": round(copy_gbps, 1),
@@ -580,6 +602,10 @@ def run_overlap_bench(args, torch, D, WG, WC):
 
 def main():
     args = parse()
+    if args.graph and args.unused_frac > 0:
+        print("bench.py: --graph and --unused-frac cannot be combined (an iteration with used flags "
+              "is not captured)", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: the library emulates the R data-parallel "
               "replicas inside one GPU's HBM and has no collective between GPUs; run with --gpus 1.",

@@ -243,10 +243,15 @@ class Lib:
     def set_launch_blocks(self, h, max_blocks: int):
         self._check(self.dll.ddpb_set_launch_blocks(h, int(max_blocks)))
 
-    def set_local_used(self, h, used: Optional[Sequence[int]]):
-        """used: R*P flags, replica-major, or None for all used."""
+    def set_local_used(self, h, used):
+        """used: R*P flags, replica-major (a sequence, or a contiguous uint8
+        NumPy array passed without copying), or None for all used."""
         if used is None:
             self._check(self.dll.ddpb_set_local_used(h, None))
+            return
+        if hasattr(used, "ctypes") and getattr(used, "dtype", None) is not None and str(used.dtype) == "uint8" \
+                and used.flags["C_CONTIGUOUS"]:
+            self._check(self.dll.ddpb_set_local_used(h, used.ctypes.data_as(C.POINTER(C.c_uint8))))
             return
         buf = (C.c_uint8 * max(len(used), 1))(*[1 if u else 0 for u in used])
         self._check(self.dll.ddpb_set_local_used(h, buf))

@@ -27,10 +27,10 @@
 //                       grid-stride over contiguous v4fs.
 //   copyback_kernel     staged step 3: averaged bucket -> R gradients.
 //   accumulate_kernel   no_sync: grad (+)= float(step) for every replica.
-//   zero_unused_kernel  bucket views: zero the slices of unused variables.
 //
-// With used flags (unused parameters) the copy-mode kernels skip variables no
-// replica used and read zeros for replicas that did not use a variable.
+// With used flags (unused parameters) the kernels read zeros for replicas that
+// did not use a variable and skip variables no replica used (bucket views:
+// write them as zeros).
 //
 // Short page names are defined in core.hpp.
 #include <hip/hip_ext.h>
@@ -153,11 +153,25 @@ __device__ __forceinline__ M used_mask(const uint8_t* used, int32_t var, int32_t
   return m;
 }
 
+// Bucket views with used flags: a variable no replica used still has its
+// bucket slices averaged (all zero-filled), so every replica's view becomes
+// +0.0. Writes zeros to `len` elements at p.
+__device__ __forceinline__ void zero_fill(float* p, int len, int lane, bool vec) {
+  int tail = 0;
+  if (vec) {
+    const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    const int n4 = len >> 2;
+    for (int i = lane; i < n4; i += 64) st4s(p + 4 * i, zero);
+    tail = n4 * 4;
+  }
+  for (int j = tail + lane; j < len; j += 64) G(p)[j] = 0.0f;
+}
+
 template <int R>
 __global__ __launch_bounds__(kBlock) void fused_mean_kernel(const Segment* __restrict__ segs, int32_t nseg,
                                                             float* const* __restrict__ grads, int32_t P,
                                                             float scale, int32_t vec_ok,
-                                                            const uint8_t* __restrict__ used,
+                                                            const uint8_t* __restrict__ used, int32_t zero_unused,
                                                             int64_t* __restrict__ stamp) {
   constexpr int U = Unroll<R>::value;
   constexpr uint32_t kAll = (1u << R) - 1;
@@ -172,10 +186,17 @@ __global__ __launch_bounds__(kBlock) void fused_mean_kernel(const Segment* __res
     for (int r = 0; r < R; ++r) p[r] = grads[static_cast<int64_t>(r) * P + g.var] + g.start;
     const int lane = lane_id();
     const uint32_t mask = used_mask<uint32_t>(used, g.var, P, R);
-    if (mask == 0) continue;                 // no replica used it: leave every gradient untouched
     uintptr_t any = 0;                       // 16-byte alignment of every replica's pointer
 #pragma unroll
     for (int r = 0; r < R; ++r) any |= reinterpret_cast<uintptr_t>(p[r]);
+    if (mask == 0) {                         // no replica used it
+      if (zero_unused) {                     // bucket views: the averaged zero slices
+        const bool vz = vec_ok && (g.flags & kSegVecStart) && (any & 15) == 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) zero_fill(p[r], len, lane, vz);
+      }
+      continue;                              // copy modes: every gradient left untouched
+    }
     if (mask != kAll) {
       // Some replicas did not use this variable: their bucket slice is zero,
       // so they add +0.0 in their place of the fixed order (their gradients
@@ -272,7 +293,7 @@ __global__ __launch_bounds__(kBlock) void fused_mean_kernel_rt(const Segment* __
                                                                float* const* __restrict__ grads, int32_t P,
                                                                int32_t R, float scale, int32_t pow2,
                                                                int32_t vec_ok, const uint8_t* __restrict__ used,
-                                                               int64_t* __restrict__ stamp) {
+                                                               int32_t zero_unused, int64_t* __restrict__ stamp) {
   stamp_begin(stamp);
   // One wavefront per segment; with a capped grid (fewer workgroups than
   // segments / 4) each wavefront strides over the remaining segments.
@@ -281,7 +302,11 @@ __global__ __launch_bounds__(kBlock) void fused_mean_kernel_rt(const Segment* __
     const int len = static_cast<int>(g.len);
     const int lane = lane_id();
     const uint64_t mask = used_mask<uint64_t>(used, g.var, P, R);
-    if (mask == 0) continue;
+    if (mask == 0) {                         // no replica used it: see fused_mean_kernel
+      if (zero_unused)
+        for (int r = 0; r < R; ++r) zero_fill(grads[static_cast<int64_t>(r) * P + g.var] + g.start, len, lane, false);
+      continue;
+    }
     int tail = 0;
     if (vec_ok && (g.flags & kSegVecStart)) {
       uintptr_t any = 0;                     // 16-byte alignment of every replica's pointer
@@ -609,23 +634,6 @@ __global__ __launch_bounds__(kBlock) void accumulate_kernel(const Segment* __res
   }
 }
 
-// gradient_as_bucket_view with unused parameters ([Li] "Handling Unused
-// Parameters"): the view of a variable a replica did not use is its slice of
-// the bucket, which must read as zeros. One wavefront per (segment, replica).
-__global__ __launch_bounds__(kBlock) void zero_unused_kernel(const Segment* __restrict__ segs, int32_t nseg,
-                                                             float* const* __restrict__ grads,
-                                                             const uint8_t* __restrict__ used, int32_t P,
-                                                             int32_t R) {
-  const int64_t w = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave_id();
-  if (w >= static_cast<int64_t>(nseg) * R) return;
-  const int r = static_cast<int>(w / nseg);
-  const Segment g = segs[w - static_cast<int64_t>(r) * nseg];
-  const int64_t k = static_cast<int64_t>(r) * P + g.var;
-  if (used[k]) return;
-  float* dst = grads[k] + g.start;
-  const int len = static_cast<int>(g.len);
-  for (int j = lane_id(); j < len; j += 64) G(dst)[j] = 0.0f;
-}
 
 // ---------------------------------------------------------------------------
 // launcher
@@ -881,16 +889,6 @@ class HipLauncher final : public Launcher {
     HIP_OK(hipEventRecord(ev_used_, compute_), "hipEventRecord(used)");
     used_recorded_ = true;
     used_active_ = true;
-    // Bucket views: zero the slices of unused (replica, variable) pairs on the
-    // compute stream, ahead of every ready event of this iteration.
-    if (mode_ == kModeBucketView && !plan_->segs.empty() && std::memchr(used, 0, n) != nullptr) {
-      const int32_t nseg = static_cast<int32_t>(plan_->segs.size());
-      const int64_t waves = static_cast<int64_t>(nseg) * R_;
-      const dim3 grid(static_cast<unsigned>((waves + kWavesPerBlock - 1) / kWavesPerBlock));
-      hipLaunchKernelGGL(zero_unused_kernel, grid, dim3(kBlock), 0, compute_, d_segs_, nseg, d_grads_, d_used_, P_,
-                         R_);
-      HIP_OK(hipGetLastError(), "launch zero_unused_kernel");
-    }
     return kOk;
   }
 
@@ -905,8 +903,12 @@ class HipLauncher final : public Launcher {
  private:
   int enqueue_bucket(int32_t b, hipStream_t s, hipEvent_t t0, hipEvent_t t1, std::string* err) {
     // Bucket-view mode runs the same fused kernel over the bucket's flat range
-    // of each replica's storage (one pseudo-variable per replica).
-    const bool view = (mode_ == kModeBucketView);
+    // of each replica's storage (one pseudo-variable per replica). With used
+    // flags it walks the per-variable segments over the views instead, so
+    // that unused replicas' slices count as zeros without being read and
+    // variables no replica used end as zeros.
+    const bool view = (mode_ == kModeBucketView) && !used_active_;
+    const int32_t zero_unused = (mode_ == kModeBucketView && used_active_) ? 1 : 0;
     const std::vector<int32_t>& first = view ? plan_->view_seg_first : plan_->seg_first;
     const int32_t s0 = first[b];
     const int32_t nseg = first[b + 1] - s0;
@@ -918,18 +920,18 @@ class HipLauncher final : public Launcher {
     const Segment* segs = (view ? d_view_segs_ : d_segs_) + s0;
     float* const* table = view ? d_view_bases_ : d_grads_;
     const int32_t tp = view ? 1 : P_;
-    const uint8_t* used = (used_active_ && !view) ? d_used_ : nullptr;   // views were zeroed at the first hook
+    const uint8_t* used = used_active_ ? d_used_ : nullptr;
     int64_t* stamp = (flags_ & 1) ? d_stamps_ + static_cast<int64_t>(b) * 4 : nullptr;
     int64_t blocks = (nseg + kWavesPerBlock - 1) / kWavesPerBlock;
     if (max_blocks_ > 0) blocks = std::min<int64_t>(blocks, max_blocks_);
     const dim3 grid(static_cast<unsigned>(blocks));
     const dim3 block(kBlock);
-    if (mode_ == kModeFused || view) {
+    if (mode_ == kModeFused || mode_ == kModeBucketView) {
       switch (R_) {
 #define DDPB_FUSED_CASE(RR)                                                                                      \
   case RR:                                                                                                       \
     hipExtLaunchKernelGGL((fused_mean_kernel<RR>), grid, block, 0, s, t0, t1, 0, segs, nseg, table, tp, scale_,   \
-                          vec_ok_, used, stamp);                                                                 \
+                          vec_ok_, used, zero_unused, stamp);                                                    \
     break;
         DDPB_FUSED_CASE(1) DDPB_FUSED_CASE(2) DDPB_FUSED_CASE(3) DDPB_FUSED_CASE(4)
         DDPB_FUSED_CASE(5) DDPB_FUSED_CASE(6) DDPB_FUSED_CASE(7) DDPB_FUSED_CASE(8)
@@ -938,7 +940,7 @@ class HipLauncher final : public Launcher {
 #undef DDPB_FUSED_CASE
         default:
           hipExtLaunchKernelGGL(fused_mean_kernel_rt, grid, block, 0, s, t0, t1, 0, segs, nseg, table, tp, R_,
-                                scale_, pow2_ ? 1 : 0, vec_ok_, used, stamp);
+                                scale_, pow2_ ? 1 : 0, vec_ok_, used, zero_unused, stamp);
       }
       HIP_OK(hipGetLastError(), "launch fused_mean_kernel");
       return kOk;

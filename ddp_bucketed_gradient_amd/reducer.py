@@ -190,7 +190,7 @@ class Reducer:
         u = np.asarray(used, dtype=bool)
         if u.shape != (self.R, self.P):
             raise ValueError(f"used flags must have shape ({self.R}, {self.P})")
-        self.lib.set_local_used(self.h, u.astype(np.uint8).ravel().tolist())
+        self.lib.set_local_used(self.h, np.ascontiguousarray(u, dtype=np.uint8).ravel())
 
     # -- diagnostics -------------------------------------------------------------------
     def launch_log(self, with_stamps: bool = False):

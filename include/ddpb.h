@@ -263,9 +263,10 @@ int ddpb_no_sync_accumulate(ddpb_t h, void* const* step_ptrs, int32_t step_dtype
  * can complete; they must not be marked again (DDPB_E_DOUBLE_READY). In the
  * reduction a replica that did not use a variable contributes zeros, and a
  * variable that no replica used keeps every replica's gradient untouched
- * (copy modes). With bucket views the unused views are zeroed on the compute
- * stream at that first hook and then averaged with their bucket, so a
- * globally unused view ends as zeros. An iteration with unused variables
+ * (copy modes). With bucket views an unused view counts as zeros in its
+ * bucket's average (it is not read) and, like every view of the bucket,
+ * receives the mean, so a view no replica used ends as zeros. An iteration
+ * with unused variables
  * records no ready order for ddpb_rebuild_buckets. DDPB_E_STATE if an
  * iteration is in progress. */
 int ddpb_set_local_used(ddpb_t h, const uint8_t* used);
