@@ -428,7 +428,10 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(const Segment* __restrict_
   stamp_end(stamp);
 }
 
-// R flat buckets -> averaged bucket; grid-stride over contiguous v4fs.
+// R flat buckets -> averaged bucket; grid-stride over contiguous v4fs, kMeanU
+// of them per thread in flight (bound-checked, as in the fused kernel).
+constexpr int kMeanU = 4;
+
 template <int R>
 __global__ __launch_bounds__(kBlock) void mean_kernel(const float* __restrict__ flat, int64_t flat_stride,
                                                       int64_t fbase, int64_t n, float* __restrict__ avg,
@@ -438,11 +441,17 @@ __global__ __launch_bounds__(kBlock) void mean_kernel(const float* __restrict__ 
   float* dst = avg + fbase;
   const int64_t n4 = n >> 2;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < n4; i += stride) {
-    v4f x[R];
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < n4; i += kMeanU * stride) {
+    v4f x[kMeanU][R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) x[r] = ld4(src + r * flat_stride + 4 * i);
-    st4(dst + 4 * i, mean4<R>(x, scale));
+    for (int u = 0; u < kMeanU; ++u)
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (i + u * stride < n4) x[u][r] = ld4(src + r * flat_stride + 4 * (i + u * stride));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kMeanU; ++u)
+      if (i + u * stride < n4) st4(dst + 4 * (i + u * stride), mean4<R>(x[u], scale));
   }
   if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
     const int64_t j = n4 * 4 + threadIdx.x;
