@@ -66,6 +66,12 @@ def parse():
     ap.add_argument("--unused-frac", type=float, default=0.0,
                     help="fraction of (replica, variable) pairs marked unused before every sync "
                          "(seeded; at least one replica uses each variable)")
+    ap.add_argument("--shuffle-params", action="store_true",
+                    help="--config 5: define the parameters in a seeded shuffled order, so that the "
+                         "reverse definition order no longer follows the backward")
+    ap.add_argument("--rebuild", action="store_true",
+                    help="--config 5: plan the first iteration as one bucket, then rebuild the buckets "
+                         "from the recorded hook order before timing")
     ap.add_argument("--hooks", choices=["each", "many"], default="each",
                     help="each = one mark_ready call per hook from Python; many = the whole hook "
                          "order in one mark_ready_many call (no binding overhead per hook)")
@@ -512,10 +518,19 @@ def run_overlap_bench(args, torch, D, WG, WC):
     torch.cuda.synchronize()
     log("inputs generated on the device")
     compute, sides = _pool_streams(torch, args.n_side)
-    red = D.Reducer([p.shape for p in params], R, cap)
-    red.bind(grads, compute_stream=compute, side_streams=sides, flags=D.BIND_TIME_LAUNCHES)
+    # definition order: the architecture's, or a seeded shuffle of it; the
+    # reducer numbers variables in definition order (dpos: layer-order index ->
+    # reducer index), while the backward below walks the layers
+    perm = WG.permutation(55, P) if args.shuffle_params else list(range(P))
+    dpos = [0] * P
+    for k, v in enumerate(perm):
+        dpos[v] = k
+    shapes_def = [params[v].shape for v in perm]
+    grads_def = [[row[v] for v in perm] for row in grads]
+    red = D.Reducer(shapes_def, R, (1 << 62) if args.rebuild else cap)
+    red.bind(grads_def, compute_stream=compute, side_streams=sides, flags=D.BIND_TIME_LAUNCHES)
     g0 = [grads[0][v].view(params[v].shape) for v in range(P)]
-    order = w.ready_order()
+    order = [dpos[v] for v in w.ready_order()]
 
     def backward(hook):
         dY = dY0
@@ -535,6 +550,17 @@ def run_overlap_bench(args, torch, D, WG, WC):
     def none(v):
         pass
 
+    def hook(v):
+        red.mark_ready(dpos[v])
+
+    if args.rebuild:                    # one iteration as a single bucket records the hook order
+        backward(hook)
+        red.finalize()
+        red.rebuild_buckets(cap)
+        red.bind(grads_def, compute_stream=compute, side_streams=sides, flags=D.BIND_TIME_LAUNCHES)
+        torch.cuda.synchronize()
+        log(f"rebuilt into {red.num_buckets} buckets from the recorded hook order")
+
     def timed(fn, reps):
         for _ in range(2):
             fn()
@@ -548,7 +574,7 @@ def run_overlap_bench(args, torch, D, WG, WC):
         return e0.elapsed_time(e1) / reps
 
     def both():
-        backward(red.mark_ready)
+        backward(hook)
         red.finalize()
 
     t_bwd = timed(lambda: backward(none), args.steps)
@@ -570,11 +596,11 @@ def run_overlap_bench(args, torch, D, WG, WC):
     # Control: one bucket (cap above S) can only launch after the last hook,
     # so nothing overlaps and the hidden fraction should be about 0.
     red.set_launch_blocks(0)
-    red1 = D.Reducer([p.shape for p in params], R, 1 << 62)
-    red1.bind(grads, compute_stream=compute, side_streams=sides, flags=D.BIND_TIME_LAUNCHES)
+    red1 = D.Reducer(shapes_def, R, 1 << 62)
+    red1.bind(grads_def, compute_stream=compute, side_streams=sides, flags=D.BIND_TIME_LAUNCHES)
 
     def both1():
-        backward(red1.mark_ready)
+        backward(lambda v: red1.mark_ready(dpos[v]))
         red1.finalize()
 
     t_red1 = timed(lambda: red1.sync(order), args.steps)
@@ -590,7 +616,8 @@ def run_overlap_bench(args, torch, D, WG, WC):
         "ms_per_step": b["t_both_ms"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16 GEMM / f32 reduce", "data": "synthetic",
         "config": {"workload": w.name, "tensors": P, "replicas": R, "bucket_cap_bytes": cap,
-                   "buckets": red.num_buckets, "tokens": T, "side_streams": args.n_side, "launch_blocks": best},
+                   "buckets": red.num_buckets, "tokens": T, "side_streams": args.n_side, "launch_blocks": best,
+                   "shuffled_definition_order": args.shuffle_params, "rebuilt": args.rebuild},
         "t_backward_ms": round(t_bwd, 4), "t_reduction_ms": b["t_reduction_ms"], "t_both_ms": b["t_both_ms"],
         "backward_TFLOPs": round(flops / (t_bwd * 1e-3) / 1e12, 1),
         "reduction_GBps": round(alg / (b["t_reduction_ms"] * 1e-3) / 1e9, 1),
