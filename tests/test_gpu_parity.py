@@ -88,10 +88,8 @@ def test_multiple_side_streams(n_side):
 
 
 def test_special_values():
-    R = 3
     vals = np.array([0.0, -0.0, 1e-45, -1e-45, 2e-45, 1.1754942e-38, 3.4e38, 3.4e38, -3.4e38,
                      np.inf, -np.inf, np.nan, 1.0, 2.0 ** 24, 1.0, -(2.0 ** 24)], dtype=np.float32)
-    host = [[np.roll(vals, r)] for r in range(R)]
     for RR in (2, 3, 8):
         host = [[np.roll(vals, r * 3 + 1).copy()] for r in range(RR)]
         for mode in (D.MODE_FUSED, D.MODE_STAGED):
@@ -101,7 +99,8 @@ def test_special_values():
             fill_from_host(grads, host)
             red.sync()
             got = snapshot(grads)
-            want, _ = _oracle_sync([vals.size], RR, 0, host, [0])
+            with np.errstate(invalid="ignore", over="ignore"):   # Inf - Inf and overflow are the point
+                want, _ = _oracle_sync([vals.size], RR, 0, host, [0])
             for r in range(RR):
                 assert_bits_equal(got[0][r], want[r][0], f"R={RR} mode={mode}")
     # subnormal results must not be flushed: (2^-149 + 2^-149) / 2
