@@ -45,7 +45,7 @@ def _host_inputs(seed, numels, R, kind="normal"):
 RAGGED = [1, 3, 4, 5, 63, 64, 65, 255, 1000, 4095, 4096, 4097, 8191, 8193, 12345, 20000, 2, 777]
 
 
-@pytest.mark.parametrize("R", [1, 2, 3, 5, 8, 16, 17, 33])
+@pytest.mark.parametrize("R", [1, 2, 3, 5, 8, 16, 17, 33, 64])
 @pytest.mark.parametrize("mode", [D.MODE_FUSED, D.MODE_STAGED])
 def test_ragged_parity(R, mode):
     numels = RAGGED
