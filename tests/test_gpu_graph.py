@@ -59,6 +59,20 @@ def test_captured_sync_replays_match_the_oracle(mode):
         for v in range(len(NUMELS)):
             for r in range(R):
                 assert_bits_equal(got[v][r], og[r][v], f"replay {rep} v={v} r={r}")
+    # eager iterations still work after capture and replays (fresh inputs)
+    host2 = _host(2, R)
+    fill_from_host(grads, host2)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(compute):
+        red.sync(order)
+    got = snapshot(grads)
+    og2 = [[h.copy() for h in row] for row in host2]
+    orc2 = OR.Reducer(NUMELS, R, cap)
+    orc2.bind(og2)
+    orc2.sync(order)
+    for v in range(len(NUMELS)):
+        for r in range(R):
+            assert_bits_equal(got[v][r], og2[r][v], f"eager after replays v={v} r={r}")
     del g
     red.close()
 
