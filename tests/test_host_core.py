@@ -124,6 +124,32 @@ def test_segment_table_covers_every_variable_once(host, numels, cap):
     assert nseg == sum((n + seg_elems - 1) // seg_elems for n in numels)
 
 
+def test_plan_of_a_tensor_beyond_int32_elements(host):
+    """A tensor of 2^31 + 9221 elements: locators, the segments that start at
+    and past 2^31, and the staged workspace are 64-bit throughout."""
+    big = (1 << 31) + 9221
+    numels = [5, big, 7]
+    for cap in (25 * MiB, 0):
+        red = _reducer(host, numels, 2, cap)
+        want = OP.compute_bucket_assignment_by_size(numels, 4, cap)
+        assert red.buckets() == want
+        loc = OP.locators(want, numels)
+        for v in range(3):
+            assert red.locator(v) == (loc[v].bucket, loc[v].intra, loc[v].offset, loc[v].length)
+        nseg, E = host.num_segments(red.h)
+        assert nseg == 1 + (big + E - 1) // E + 1
+        b1, _, off1, _ = red.locator(1)
+        first, count = host.get_bucket_segments(red.h, b1)
+        k0 = first + (1 if cap else 0)                # the 7-element variable comes first at 25 MiB
+        at_edge = host.get_segment(red.h, k0 + (1 << 31) // E)
+        assert at_edge == (1, b1, 1 << 31, E, off1 + (1 << 31))
+        last = host.get_segment(red.h, k0 + (big - 1) // E)
+        assert last == (1, b1, (big - 1) // E * E, big - (big - 1) // E * E, off1 + (big - 1) // E * E)
+        flat = sum((n + 63) // 64 * 64 for n in OP.bucket_numels(want, numels))
+        assert red.workspace_bytes(D.MODE_STAGED) == 3 * flat * 4
+        assert host.view_storage_elems(red.h) == flat
+
+
 def test_workspace_bytes(host):
     numels = [10, 100, 3]
     red = _reducer(host, numels, 4, 0)
