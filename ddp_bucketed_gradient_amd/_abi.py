@@ -29,6 +29,7 @@ SYMBOLS = [
     "ddpb_bind", "ddpb_ensure_prior_reduction_finished", "ddpb_mark_ready", "ddpb_mark_ready_many",
     "ddpb_finalize", "ddpb_set_sync", "ddpb_no_sync_accumulate", "ddpb_reset", "ddpb_get_launch_log",
     "ddpb_get_launch_times", "ddpb_device_clock_hz", "ddpb_last_error", "ddpb_set_launch_blocks",
+    "ddpb_set_workgroups_per_cu",
     "ddpb_view_storage_elems", "ddpb_get_view_offset", "ddpb_bind_bucket_views",
     "ddpb_rebuild_buckets", "ddpb_get_ready_order", "ddpb_set_local_used",
 ]
@@ -67,6 +68,7 @@ def _sig(lib):
         "ddpb_get_launch_times": [vp, i32, C.POINTER(C.c_float), C.POINTER(C.c_float), i32, P32],
         "ddpb_device_clock_hz": [vp, P64],
         "ddpb_set_launch_blocks": [vp, i32],
+        "ddpb_set_workgroups_per_cu": [vp, i32],
         "ddpb_set_local_used": [vp, C.POINTER(C.c_uint8)],
         "ddpb_rebuild_buckets": [vp, i64],
         "ddpb_get_ready_order": [vp, P32, i32, P32],
@@ -242,6 +244,9 @@ class Lib:
 
     def set_launch_blocks(self, h, max_blocks: int):
         self._check(self.dll.ddpb_set_launch_blocks(h, int(max_blocks)))
+
+    def set_workgroups_per_cu(self, h, n: int):
+        self._check(self.dll.ddpb_set_workgroups_per_cu(h, int(n)))
 
     def set_local_used(self, h, used):
         """used: R*P flags, replica-major (a sequence, or a contiguous uint8

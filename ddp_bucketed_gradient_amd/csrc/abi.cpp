@@ -316,6 +316,12 @@ int ddpb_set_launch_blocks(ddpb_t h, int32_t max_blocks) {
   return DDPB_OK;
 }
 
+int ddpb_set_workgroups_per_cu(ddpb_t h, int32_t n) {
+  if (!h || n < 0 || n > 2) return fail(DDPB_E_ARG, "set_workgroups_per_cu: n must be 0, 1 or 2");
+  std::string err;
+  return pass(h->red.launcher()->set_workgroups_per_cu(n, &err), err);
+}
+
 int ddpb_device_clock_hz(ddpb_t h, int64_t* hz) {
   if (!h || !hz) return fail(DDPB_E_ARG, "device_clock_hz: NULL argument");
   std::string err;

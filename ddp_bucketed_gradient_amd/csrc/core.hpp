@@ -131,6 +131,8 @@ class Launcher {
   virtual int clock_hz(int64_t* hz, std::string* err) = 0;
   // Caps the workgroups of each reduction launch (0 = one per four segments).
   virtual void set_max_blocks(int32_t n) = 0;
+  // At most n fused-kernel workgroups per compute unit (0 = registers decide).
+  virtual int set_workgroups_per_cu(int32_t n, std::string* err) = 0;
   // Used flags for the launches that follow (R * P replica-major, and the OR
   // over replicas per variable), or NULL for "all used". Ordered on the
   // compute stream before the next launch's ready event.

@@ -167,7 +167,15 @@ __device__ __forceinline__ void zero_fill(float* p, int len, int lane, bool vec)
   for (int j = tail + lane; j < len; j += 64) G(p)[j] = 0.0f;
 }
 
-template <int R>
+// MASKED = false compiles the used-flag paths out: 168 VGPRs instead of 256
+// VGPRs + 44 AGPRs, so up to three of its waves share a SIMD. Run beside a
+// bf16 GEMM backward with no limit on workgroups per CU it hid 0.16 of the
+// reduction against 0.09-0.11 for one workgroup per CU. The launcher uses it
+// for launches without used flags when workgroups may share CUs
+// (ddpb_set_workgroups_per_cu 0 or 2). At one workgroup per CU the general
+// build streams 0.4 % faster (BERT-large sync: 5,757 vs 5,734 GB/s, three runs
+// each on one box) and is used instead.
+template <int R, bool MASKED>
 __global__ __launch_bounds__(kBlock) void fused_mean_kernel(const Segment* __restrict__ segs, int32_t nseg,
                                                             float* const* __restrict__ grads, int32_t P,
                                                             float scale, int32_t vec_ok,
@@ -185,11 +193,11 @@ __global__ __launch_bounds__(kBlock) void fused_mean_kernel(const Segment* __res
 #pragma unroll
     for (int r = 0; r < R; ++r) p[r] = grads[static_cast<int64_t>(r) * P + g.var] + g.start;
     const int lane = lane_id();
-    const uint32_t mask = used_mask<uint32_t>(used, g.var, P, R);
+    const uint32_t mask = MASKED ? used_mask<uint32_t>(used, g.var, P, R) : kAll;
     uintptr_t any = 0;                       // 16-byte alignment of every replica's pointer
 #pragma unroll
     for (int r = 0; r < R; ++r) any |= reinterpret_cast<uintptr_t>(p[r]);
-    if (mask == 0) {                         // no replica used it
+    if (MASKED && mask == 0) {               // no replica used it
       if (zero_unused) {                     // bucket views: the averaged zero slices
         const bool vz = vec_ok && (g.flags & kSegVecStart) && (any & 15) == 0;
 #pragma unroll
@@ -197,7 +205,7 @@ __global__ __launch_bounds__(kBlock) void fused_mean_kernel(const Segment* __res
       }
       continue;                              // copy modes: every gradient left untouched
     }
-    if (mask != kAll) {
+    if (MASKED && mask != kAll) {
       // Some replicas did not use this variable: their bucket slice is zero,
       // so they add +0.0 in their place of the fixed order (their gradients
       // are not read). The mask is the same for the whole wavefront.
@@ -494,7 +502,8 @@ __global__ __launch_bounds__(kBlock) void copyback_kernel(const Segment* __restr
     const int lane = lane_id();
     const float* src = avg + fbase + g.boff;
     uintptr_t any = 0;
-    for (int r = 0; r < R; ++r) any |= reinterpret_cast<uintptr_t>(grads[static_cast<int64_t>(r) * P + g.var] + g.start);
+    for (int r = 0; r < R; ++r)
+      any |= reinterpret_cast<uintptr_t>(grads[static_cast<int64_t>(r) * P + g.var] + g.start);
     const bool vec = vec_ok && (g.flags & kSegVecBoth) == kSegVecBoth && (any & 15) == 0;
     int tail = 0;
     if (vec) {
@@ -748,7 +757,7 @@ class HipLauncher final : public Launcher {
       for (auto& e : ev_t0_) HIP_OK(hipEventCreateWithFlags(&e, hipEventDisableSystemFence), "hipEventCreate");
       for (auto& e : ev_t1_) HIP_OK(hipEventCreateWithFlags(&e, hipEventDisableSystemFence), "hipEventCreate");
     }
-    return kOk;
+    return update_lds_reserve(err);
   }
 
   int launch(int32_t first, int32_t last, int64_t iteration, std::string* err) override {
@@ -877,6 +886,11 @@ class HipLauncher final : public Launcher {
 
   void set_max_blocks(int32_t n) override { max_blocks_ = n; }
 
+  int set_workgroups_per_cu(int32_t n, std::string* err) override {
+    wg_per_cu_ = n;
+    return update_lds_reserve(err);
+  }
+
   int set_used(const uint8_t* used, const uint8_t* global, std::string* err) override {
     (void)global;                  // the kernels derive it from the per-replica flags
     if (used == nullptr) {
@@ -936,11 +950,16 @@ class HipLauncher final : public Launcher {
     const dim3 grid(static_cast<unsigned>(blocks));
     const dim3 block(kBlock);
     if (mode_ == kModeFused || mode_ == kModeBucketView) {
+      const bool compact = (used == nullptr) && wg_per_cu_ != 1;
       switch (R_) {
 #define DDPB_FUSED_CASE(RR)                                                                                      \
   case RR:                                                                                                       \
-    hipExtLaunchKernelGGL((fused_mean_kernel<RR>), grid, block, 0, s, t0, t1, 0, segs, nseg, table, tp, scale_,   \
-                          vec_ok_, used, zero_unused, stamp);                                                    \
+    if (!compact)                                                                                                \
+      hipExtLaunchKernelGGL((fused_mean_kernel<RR, true>), grid, block, lds_reserve_, s, t0, t1, 0, segs, nseg,  \
+                            table, tp, scale_, vec_ok_, used, zero_unused, stamp);                               \
+    else                                                                                                         \
+      hipExtLaunchKernelGGL((fused_mean_kernel<RR, false>), grid, block, lds_reserve_, s, t0, t1, 0, segs,      \
+                            nseg, table, tp, scale_, vec_ok_, used, zero_unused, stamp);                         \
     break;
         DDPB_FUSED_CASE(1) DDPB_FUSED_CASE(2) DDPB_FUSED_CASE(3) DDPB_FUSED_CASE(4)
         DDPB_FUSED_CASE(5) DDPB_FUSED_CASE(6) DDPB_FUSED_CASE(7) DDPB_FUSED_CASE(8)
@@ -948,8 +967,8 @@ class HipLauncher final : public Launcher {
         DDPB_FUSED_CASE(13) DDPB_FUSED_CASE(14) DDPB_FUSED_CASE(15) DDPB_FUSED_CASE(16)
 #undef DDPB_FUSED_CASE
         default:
-          hipExtLaunchKernelGGL(fused_mean_kernel_rt, grid, block, 0, s, t0, t1, 0, segs, nseg, table, tp, R_,
-                                scale_, pow2_ ? 1 : 0, vec_ok_, used, zero_unused, stamp);
+          hipExtLaunchKernelGGL(fused_mean_kernel_rt, grid, block, lds_reserve_, s, t0, t1, 0, segs, nseg, table, tp,
+                                R_, scale_, pow2_ ? 1 : 0, vec_ok_, used, zero_unused, stamp);
       }
       HIP_OK(hipGetLastError(), "launch fused_mean_kernel");
       return kOk;
@@ -983,6 +1002,21 @@ class HipLauncher final : public Launcher {
     hipExtLaunchKernelGGL(copyback_kernel, grid, block, 0, s, nullptr, t1, 0, segs, nseg, d_grads_, P_, R_, avg_,
                           fbase, vec_ok_, used, static_cast<int64_t*>(nullptr));
     HIP_OK(hipGetLastError(), "launch copyback_kernel");
+    return kOk;
+  }
+
+  // A CU holds at most wg_per_cu_ fused-kernel workgroups when each reserves
+  // more than 1/(wg_per_cu_ + 1) of the CU's LDS (the kernels use none).
+  int update_lds_reserve(std::string* err) {
+    lds_reserve_ = 0;
+    if (wg_per_cu_ == 0 || plan_ == nullptr) return kOk;      // (computed again at bind)
+    int per_cu = 0, per_block = 0;
+    HIP_OK(hipDeviceGetAttribute(&per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, device_),
+           "LDS per CU");
+    HIP_OK(hipDeviceGetAttribute(&per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, device_),
+           "LDS per workgroup");
+    const size_t want = (static_cast<size_t>(per_cu) / (wg_per_cu_ + 1) + 256 + 255) / 256 * 256;
+    lds_reserve_ = std::min<size_t>(want, static_cast<size_t>(per_block));
     return kOk;
   }
 
@@ -1028,6 +1062,8 @@ class HipLauncher final : public Launcher {
   float scale_ = 1.0f;
   int32_t vec_ok_ = 1;
   int32_t max_blocks_ = 0;     // cap on workgroups per reduction launch (0 = none)
+  int32_t wg_per_cu_ = 1;      // fused-kernel workgroups per CU (0 = no limit)
+  size_t lds_reserve_ = 0;     // dynamic LDS per fused-kernel workgroup that enforces it
   hipStream_t compute_ = nullptr;
   std::vector<hipStream_t> side_;
   std::vector<uint8_t> side_used_;

@@ -203,6 +203,11 @@ class Reducer:
         """Cap the workgroups per reduction launch (0 = whole GPU)."""
         self.lib.set_launch_blocks(self.h, max_blocks)
 
+    def set_workgroups_per_cu(self, n: int):
+        """At most n (1 or 2) reduction workgroups per compute unit; 0 = no
+        limit (denser sharing with concurrent backward kernels)."""
+        self.lib.set_workgroups_per_cu(self.h, n)
+
     def device_clock_hz(self) -> int:
         return self.lib.device_clock_hz(self.h)
 

@@ -423,6 +423,42 @@ def test_capped_grid_parity(mode, blocks):
             assert_bits_equal(got[v][r], want[r][v], f"blocks={blocks} v={v} r={r}")
 
 
+@pytest.mark.parametrize("R", [8, 20])
+@pytest.mark.parametrize("wg", [0, 1, 2])
+@pytest.mark.parametrize("flags", [False, True])
+def test_workgroups_per_cu_parity(R, wg, flags):
+    """The LDS reservation that bounds reduction workgroups per CU, for the
+    kernels with and without used flags and the generic-R kernel: same bits
+    as the oracle, several buckets, two side streams."""
+    numels = RAGGED + [70000, 3, 131072]
+    say(f"workgroups_per_cu={wg} R={R} flags={flags}")
+    red = D.Reducer([(n,) for n in numels], R, 4 * 30000)
+    red.set_workgroups_per_cu(wg)
+    grads = alloc_grads(numels, R)
+    red.bind(grads)
+    orc = OR.Reducer(numels, R, 4 * 30000)
+    host = _host_inputs(60 + wg + 3 * R, numels, R)
+    og = [[np.array(h, np.float32, copy=True) for h in row] for row in host]
+    orc.bind(og)
+    fill_from_host(grads, host)
+    order = WG.permutation(78, len(numels))
+    if flags:
+        rng = np.random.default_rng(wg + R)
+        used = rng.random((R, len(numels))) < 0.7
+        red.set_local_used(used)
+        orc.set_local_used(used)
+        G = used.any(axis=0)
+        order = [v for v in order if G[v]]
+    red.sync(order)
+    orc.sync(order)
+    got = snapshot(grads)
+    assert red.launch_log() == orc.launch_log
+    for v in range(len(numels)):
+        for r in range(R):
+            assert_bits_equal(got[v][r], og[r][v], f"wg={wg} R={R} v={v} r={r}")
+    red.close()
+
+
 def _mlp_backward(params, g0, X, H, W1, W2, dY0, hook):
     """Backward of [Linear(d, f), Linear(f, d)] blocks in bf16, last layer
     first; fp32 gradients of replica 0 are written in place."""

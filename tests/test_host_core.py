@@ -150,6 +150,16 @@ def test_plan_of_a_tensor_beyond_int32_elements(host):
         assert host.view_storage_elems(red.h) == flat
 
 
+def test_workgroups_per_cu_arguments(host):
+    red = _reducer(host, [10, 20], 2, 0)
+    for n in (0, 1, 2):
+        red.set_workgroups_per_cu(n)
+    for n in (-1, 3):
+        with pytest.raises(D.DdpbError) as e:
+            red.set_workgroups_per_cu(n)
+        assert e.value.code == D.E_ARG
+
+
 def test_workspace_bytes(host):
     numels = [10, 100, 3]
     red = _reducer(host, numels, 4, 0)
