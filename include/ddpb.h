@@ -186,19 +186,19 @@ int ddpb_bind_bucket_views(ddpb_t h, void* const* replica_storage, int64_t stora
  * depend on the cap. May be called at any time; applies to later launches. */
 int ddpb_set_launch_blocks(ddpb_t h, int32_t max_blocks);
 
-/* At most n workgroups of the fused reduction kernels (fused and bucket-view
+/* At most n workgroups of the reduction kernels (fused, bucket-view and staged
  * modes) share one compute unit, counting every launch in flight: n = 1 (the
  * default) or 2, or 0 for no limit beyond the kernels' register budget (three
- * per CU for the kernel used without used flags). One per CU gives the highest
- * throughput for a synchronisation running alone: a CU holding two workgroups
- * of one launch finishes after the others. No limit lets the reduction share
- * CUs more densely with concurrent backward kernels and hides more of it
- * behind them ([PDTI] §3.1: collectives occupy the compute units of the
- * compute they overlap). Enforced by reserving, per workgroup, more than
- * 1/(n+1) of a CU's LDS (the kernels use none); a backward GEMM workgroup
- * that needs less than the rest still fits beside one. Results do not depend
- * on it. May be called at any time; applies to later launches. Returns
- * DDPB_E_ARG for n outside 0..2. */
+ * per CU for the fused kernel used without used flags). One per CU gives the
+ * highest throughput for a synchronisation running alone: a CU holding two
+ * workgroups of one launch finishes after the others. No limit lets the
+ * reduction share CUs more densely with concurrent backward kernels, which hid
+ * more of it behind a 48-bucket MLP backward ([PDTI] §3.1: collectives occupy
+ * the compute units of the compute they overlap). Enforced by reserving, per
+ * workgroup, more than 1/(n+1) of a CU's LDS (the kernels use none). The
+ * no_sync accumulation always runs one workgroup per CU. Results do not
+ * depend on it. May be called at any time; applies to later launches.
+ * Returns DDPB_E_ARG for n outside 0..2. */
 int ddpb_set_workgroups_per_cu(ddpb_t h, int32_t n);
 
 /* ---------------------------------------------------------------------------
