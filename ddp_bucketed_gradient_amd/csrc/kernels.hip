@@ -32,6 +32,12 @@
 // did not use a variable and skip variables no replica used (bucket views:
 // write them as zeros).
 //
+// Occupancy: a CU runs one workgroup of these streaming kernels at a time by
+// default (each workgroup reserves more than half the CU's LDS, which the
+// kernels do not use). More concurrent waves per CU only add DRAM streams and
+// let one CU fall behind the others; ddpb_set_workgroups_per_cu relaxes it for
+// the reduction kernels when they share the GPU with a backward.
+//
 // Short page names are defined in core.hpp.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -1020,8 +1026,10 @@ class HipLauncher final : public Launcher {
            "LDS per CU");
     HIP_OK(hipDeviceGetAttribute(&per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, device_),
            "LDS per workgroup");
+    // a CU holds at least what one workgroup may use (gfx950: 160 KiB both)
+    const size_t cu_lds = static_cast<size_t>(std::max(per_cu, per_block));
     auto reserve = [&](int n) {
-      const size_t want = (static_cast<size_t>(per_cu) / (n + 1) + 256 + 255) / 256 * 256;
+      const size_t want = (cu_lds / (n + 1) + 256 + 255) / 256 * 256;
       return std::min<size_t>(want, static_cast<size_t>(per_block));
     };
     lds_one_per_cu_ = reserve(1);
