@@ -17,7 +17,8 @@ Other workloads (not the default line): ``--config 2`` (ResNet-50 shapes),
 ``--config 4`` (no_sync: BERT-base shapes, R=16, 8 bf16 micro-steps, then one
 sync), ``--config 5`` (overlap with a bf16 MLP backward), ``--cap-mib``,
 ``--mode staged|view``, ``--n-side``, ``--graph`` (replays of one captured
-sync), ``--hooks many`` (all hooks in one call).
+sync), ``--hooks many`` (all hooks in one call), ``--unused-frac`` (used
+flags), ``--wg-per-cu`` (reduction workgroups per compute unit).
 """
 from __future__ import annotations
 
