@@ -1,6 +1,5 @@
 """GPU parity after a ready-order bucket rebuild, in the copying mode and in
 the bucket-view mode, against the oracle's rebuild on the same inputs."""
-import numpy as np
 import pytest
 import torch
 

@@ -3,7 +3,6 @@ ABI (host-only build): the view offsets follow the oracle's plan, and the
 state machine behaves as in the copying mode."""
 import os
 
-import numpy as np
 import pytest
 
 import ddp_bucketed_gradient_amd as D

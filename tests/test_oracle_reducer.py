@@ -8,7 +8,6 @@ import pytest
 
 from conftest import load_golden
 from oracle import reducer as OR
-from oracle import plan as OP
 from workloads import gen as WG
 
 MiB = 1 << 20

@@ -4,8 +4,8 @@ Workload definitions only; nothing here plans buckets or reduces anything.
 """
 from __future__ import annotations
 
-from dataclasses import dataclass, field
-from typing import Callable, List, Optional
+from dataclasses import dataclass
+from typing import Callable, List
 
 from . import shapes as S
 
