@@ -124,9 +124,13 @@ def union_length(starts, durs) -> float:
     return total
 
 
-def hbm_copy_ceiling(torch, gb: float = 2.0) -> float:
-    """Plain device-to-device copy bandwidth (read + write bytes / time)."""
-    n = int(gb * 1e9 / 4)
+COPY_CEILING_BYTES = 4_000_000_000
+
+
+def hbm_copy_ceiling(torch, nbytes: int = COPY_CEILING_BYTES) -> float:
+    """Plain device-to-device copy bandwidth of nbytes (read + write bytes /
+    time), the practical ceiling the sync is also compared with."""
+    n = nbytes // 4
     a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
     b = torch.empty_like(a)
     for _ in range(3):
@@ -407,6 +411,7 @@ def run_sync_bench(args, torch, D, WG, WC):
                    "alg_bytes_per_step": alg},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "hbm_copy_GBps": round(copy_gbps, 1),
+        "pct_of_copy_ceiling": round(100 * value / copy_gbps, 2),
         "ms_per_step_events": round(ev_ms, 4),
         "ms_per_sync_median": round(med_ms, 4),
         "ms_per_sync_p95": round(p95_ms, 4),
