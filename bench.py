@@ -13,7 +13,8 @@ Algorithmic bytes per step = 2 * R * S (every replica's gradients read once and
 written once; S = bytes of one replica's gradients). ``value`` is that divided
 by the wall-clock time per step.
 
-Other workloads (not the default line): ``--config 2`` (ResNet-50 shapes),
+Other workloads (not the default line): ``--config 1`` (nn.Linear(10,10), R=2:
+microseconds per synchronised sync), ``--config 2`` (ResNet-50 shapes),
 ``--config 4`` (no_sync: BERT-base shapes, R=16, 8 bf16 micro-steps, then one
 sync), ``--config 5`` (overlap with a bf16 MLP backward), ``--cap-mib``,
 ``--mode staged|view``, ``--n-side``, ``--graph`` (replays of one captured
@@ -45,7 +46,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=3, choices=[2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--cap-mib", type=float, default=None)
     ap.add_argument("--mode", choices=["fused", "staged", "view"], default="fused",
                     help="view = gradient_as_bucket_view (gradients live in flat bucket storages)")
@@ -649,6 +650,58 @@ def run_overlap_bench(args, torch, D, WG, WC):
     }
 
 
+def run_latency_bench(args, torch, D, WG, WC):
+    """nn.Linear(10,10) gradients (bias 10 + weight 100 floats), R = 2, one
+    440-byte bucket: a latency-bound sync, reported in microseconds. Each
+    timed sync is followed by a device synchronisation, so the figure is
+    hooks + launch + kernel + join as a caller waiting for the result sees it."""
+    w = WC.LINEAR10
+    params = w.params()
+    numels = w.numels()
+    R = w.R
+    compute, sides = _pool_streams(torch, args.n_side)
+    grads = [[torch.empty(n, dtype=torch.float32, device="cuda") for n in numels] for _ in range(R)]
+    for r in range(R):
+        for v, n in enumerate(numels):
+            WG.normal(WG.seed_of(1, r, v), n, "cuda", out=grads[r][v])
+    red = D.Reducer([p.shape for p in params], R, w.cap_bytes)
+    red.bind(grads, compute_stream=compute, side_streams=sides)
+    order = w.ready_order()
+    for _ in range(args.warmup):
+        red.sync(order)
+        torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        red.sync(order)
+        torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) * 1e6 / args.steps
+    log(f"timed {args.steps} syncs: {us:.1f} us each (synchronised)")
+    # the oracle on the same sync, one host core (cpu_baseline leg)
+    from oracle import reducer as OR
+    host = [[g.cpu().numpy().copy() for g in row] for row in grads]
+    orc = OR.Reducer(numels, R, w.cap_bytes)
+    orc.bind(host)
+    n_cpu = 0
+    c0 = time.perf_counter()
+    while time.perf_counter() - c0 < 1.0:
+        orc.sync(order)
+        n_cpu += 1
+    cpu_us = (time.perf_counter() - c0) * 1e6 / n_cpu
+    return {
+        "metric": f"us per bucketed sync (latency bound), {w.name}",
+        "value": round(us, 2), "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 5), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "tensors": len(numels), "replicas": R, "bucket_cap_bytes": w.cap_bytes,
+                   "buckets": red.num_buckets, "bytes_per_replica": 4 * sum(numels),
+                   "side_streams": args.n_side},
+        "roofline": None,
+        "cpu_baseline": {"value": round(cpu_us, 2), "unit": "us", "cores": 1, "kind": "oracle",
+                         "sample": f"whole workload, {n_cpu} syncs"},
+    }
+
+
 def main():
     args = parse()
     if args.graph and args.unused_frac > 0:
@@ -667,7 +720,9 @@ def main():
     import ddp_bucketed_gradient_amd as D
     from workloads import gen as WG, configs as WC
     torch.cuda.set_device(0)
-    if args.config in (2, 3):
+    if args.config == 1:
+        out = run_latency_bench(args, torch, D, WG, WC)
+    elif args.config in (2, 3):
         out = run_sync_bench(args, torch, D, WG, WC)
     elif args.config == 4:
         out = run_nosync_bench(args, torch, D, WG, WC)
