@@ -426,16 +426,17 @@ def test_capped_grid_parity(mode, blocks):
 @pytest.mark.parametrize("R", [8, 20])
 @pytest.mark.parametrize("wg", [0, 1, 2])
 @pytest.mark.parametrize("flags", [False, True])
-def test_workgroups_per_cu_parity(R, wg, flags):
+@pytest.mark.parametrize("mode", [D.MODE_FUSED, D.MODE_STAGED])
+def test_workgroups_per_cu_parity(R, wg, flags, mode):
     """The LDS reservation that bounds reduction workgroups per CU, for the
-    kernels with and without used flags and the generic-R kernel: same bits
-    as the oracle, several buckets, two side streams."""
+    fused kernels with and without used flags, the generic-R kernel and the
+    staged trio: same bits as the oracle, several buckets, two side streams."""
     numels = RAGGED + [70000, 3, 131072]
-    say(f"workgroups_per_cu={wg} R={R} flags={flags}")
+    say(f"workgroups_per_cu={wg} R={R} flags={flags} mode={mode}")
     red = D.Reducer([(n,) for n in numels], R, 4 * 30000)
     red.set_workgroups_per_cu(wg)
     grads = alloc_grads(numels, R)
-    red.bind(grads)
+    red.bind(grads, mode=mode)
     orc = OR.Reducer(numels, R, 4 * 30000)
     host = _host_inputs(60 + wg + 3 * R, numels, R)
     og = [[np.array(h, np.float32, copy=True) for h in row] for row in host]
