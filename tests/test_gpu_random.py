@@ -1,7 +1,7 @@
 """Randomized GPU parity: seeded configurations that mix the replica count
 (templated and generic-R kernels), ragged and empty tensors, bucket caps, the
-fused, staged and bucket-view modes, capped launch grids, used flags and
-permuted hook orders. Every replica's every gradient must equal the oracle's
+fused, staged and bucket-view modes, capped launch grids, workgroups per CU,
+used flags and permuted hook orders. Every replica's every gradient must equal the oracle's
 bit for bit, over two iterations with fresh inputs."""
 import numpy as np
 import pytest
@@ -32,14 +32,15 @@ def _config(seed):
     mode = str(rng.choice(["fused", "staged", "view"]))
     blocks = int(rng.choice([0, 0, 1, 3]))
     with_flags = bool(rng.integers(0, 2))
-    return rng, numels, R, cap, mode, blocks, with_flags
+    wg = int(rng.choice([0, 1, 1, 2]))            # reduction workgroups per CU
+    return rng, numels, R, cap, mode, blocks, with_flags, wg
 
 
 @pytest.mark.parametrize("seed", range(100))
 def test_random_configuration(seed):
-    rng, numels, R, cap, mode, blocks, with_flags = _config(seed)
+    rng, numels, R, cap, mode, blocks, with_flags, wg = _config(seed)
     P = len(numels)
-    say(f"random seed={seed} P={P} R={R} cap={cap} mode={mode} blocks={blocks} flags={with_flags}")
+    say(f"random seed={seed} P={P} R={R} cap={cap} mode={mode} blocks={blocks} flags={with_flags} wg={wg}")
     red = D.Reducer([(n,) for n in numels], R, cap)
     view = mode == "view"
     orc = OR.Reducer(numels, R, cap, gradient_as_bucket_view=view)
@@ -53,6 +54,7 @@ def test_random_configuration(seed):
         og = [[np.zeros(n, np.float32) for n in numels] for _ in range(R)]
         orc.bind(og)
     red.set_launch_blocks(blocks)
+    red.set_workgroups_per_cu(wg)
     for it in range(2):
         host = [[WG.normal(WG.seed_of(9, r, v, (seed * 2 + it) % 100), n).numpy() for v, n in enumerate(numels)]
                 for r in range(R)]
