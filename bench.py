@@ -449,6 +449,8 @@ def run_nosync_bench(args, torch, D, WG, WC):
     compute, sides = _pool_streams(torch, args.n_side)
     red = D.Reducer([p.shape for p in w.params()], R, w.cap_bytes)
     red.bind(grads, compute_stream=compute, side_streams=sides, flags=D.BIND_TIME_LAUNCHES)
+    wg_per_cu = 1 if args.wg_per_cu is None else args.wg_per_cu
+    red.set_workgroups_per_cu(wg_per_cu)
     order = w.ready_order()
     acc_ms = []
 
@@ -493,7 +495,8 @@ def run_nosync_bench(args, torch, D, WG, WC):
         "ms_per_step": round(wall_ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "tensors": P, "params": N, "replicas": R, "micro_steps": k,
-                   "step_dtype": "bf16", "buckets": red.num_buckets, "alg_bytes_per_step": alg},
+                   "step_dtype": "bf16", "buckets": red.num_buckets, "workgroups_per_cu": wg_per_cu,
+                   "alg_bytes_per_step": alg},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "accumulate_first_ms": round(sum(acc_first) / len(acc_first), 4),
         "accumulate_ms": round(avg_rest, 4), "sync_busy_ms_last": round(sync_ms, 4),
@@ -670,6 +673,8 @@ def run_latency_bench(args, torch, D, WG, WC):
             WG.normal(WG.seed_of(1, r, v), n, "cuda", out=grads[r][v])
     red = D.Reducer([p.shape for p in params], R, w.cap_bytes)
     red.bind(grads, compute_stream=compute, side_streams=sides)
+    wg_per_cu = 1 if args.wg_per_cu is None else args.wg_per_cu
+    red.set_workgroups_per_cu(wg_per_cu)
     order = w.ready_order()
     for _ in range(args.warmup):
         red.sync(order)
@@ -699,7 +704,7 @@ def run_latency_bench(args, torch, D, WG, WC):
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "tensors": len(numels), "replicas": R, "bucket_cap_bytes": w.cap_bytes,
                    "buckets": red.num_buckets, "bytes_per_replica": 4 * sum(numels),
-                   "side_streams": args.n_side},
+                   "side_streams": args.n_side, "workgroups_per_cu": wg_per_cu},
         "roofline": None,
         "cpu_baseline": {"value": round(cpu_us, 2), "unit": "us", "cores": 1, "kind": "oracle",
                          "sample": f"whole workload, {n_cpu} syncs"},
