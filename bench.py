@@ -16,7 +16,9 @@ by the wall-clock time per step.
 Other workloads (not the default line): ``--config 1`` (nn.Linear(10,10), R=2:
 microseconds per synchronised sync), ``--config 2`` (ResNet-50 shapes),
 ``--config 4`` (no_sync: BERT-base shapes, R=16, 8 bf16 micro-steps, then one
-sync), ``--config 5`` (overlap with a bf16 MLP backward), ``--cap-mib``,
+sync), ``--config 5`` (overlap with a bf16 MLP backward), ``--config 6`` (the
+blog's 48 MiB payload, R=4, as 12 x 4 MiB or, with ``--blog-param-mib 1``,
+48 x 1 MiB parameters; cap 4 MiB unless ``--cap-mib``), ``--cap-mib``,
 ``--mode staged|view``, ``--n-side``, ``--graph`` (replays of one captured
 sync), ``--hooks many`` (all hooks in one call), ``--unused-frac`` (used
 flags), ``--wg-per-cu`` (reduction workgroups per compute unit).
@@ -46,7 +48,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5, 6])
+    ap.add_argument("--blog-param-mib", type=int, default=4, choices=[1, 4],
+                    help="--config 6: the 48 MiB payload as 12 x 4 MiB or 48 x 1 MiB parameters")
     ap.add_argument("--cap-mib", type=float, default=None)
     ap.add_argument("--mode", choices=["fused", "staged", "view"], default="fused",
                     help="view = gradient_as_bucket_view (gradients live in flat bucket storages)")
@@ -216,6 +220,8 @@ def cpu_baseline_threads(w, host_in, nvars_sample, min_seconds, threads):
 def run_sync_bench(args, torch, D, WG, WC):
     if args.config == 2:
         w = WC.RESNET50
+    elif args.config == 6:
+        w = WC.BLOG_COARSE4 if args.blog_param_mib == 4 else WC.BLOG_FINE1
     else:
         w = WC.BERT_LARGE
     if args.cap_mib is not None:
@@ -731,7 +737,7 @@ def main():
     torch.cuda.set_device(0)
     if args.config == 1:
         out = run_latency_bench(args, torch, D, WG, WC)
-    elif args.config in (2, 3):
+    elif args.config in (2, 3, 6):
         out = run_sync_bench(args, torch, D, WG, WC)
     elif args.config == 4:
         out = run_nosync_bench(args, torch, D, WG, WC)

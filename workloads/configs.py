@@ -39,6 +39,9 @@ RESNET50 = Workload(2, "resnet50_r8", S.resnet50, R=8)
 BERT_LARGE = Workload(3, "bert_large_r8_cap25", S.bert_large, R=8)
 BERT_BASE_NOSYNC = Workload(4, "bert_base_r16_nosync_k8", S.bert_base, R=16,
                             micro_steps=8, step_dtype="bf16")
+# the blog's 48 MiB payload per rank on 4 ranks, as 12 x 4 MiB or 48 x 1 MiB parameters
+BLOG_COARSE4 = Workload(6, "blog48mib_12x4mib_r4", S.blog_coarse4, R=4, cap_bytes=4 * MiB)
+BLOG_FINE1 = Workload(6, "blog48mib_48x1mib_r4", S.blog_fine1, R=4, cap_bytes=4 * MiB)
 MLP_OVERLAP = Workload(5, "mlp24_d2048_f8192_r8_overlap", S.mlp, R=8,
                        note="bf16 backward GEMMs over 8192 tokens on the compute stream")
 
