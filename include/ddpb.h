@@ -56,8 +56,11 @@ enum {
 
 /* flags for ddpb_bind */
 enum {
-  DDPB_BIND_DEVICE_TIMESTAMPS = 1, /* kernels stamp start/end device clock into the launch log */
-  DDPB_BIND_TIME_LAUNCHES = 2      /* hipEvents around each bucket's kernels (ddpb_get_launch_times) */
+  DDPB_BIND_DEVICE_TIMESTAMPS = 1, /* kernels stamp start/end device clock into the launch log; a
+                                      diagnostic: each workgroup's closing fence and counter update
+                                      cost about 10 % of the throughput of a BERT-large sync */
+  DDPB_BIND_TIME_LAUNCHES = 2      /* hipEvents around each bucket's kernels (ddpb_get_launch_times);
+                                      about 0.8 % of that throughput */
 };
 
 /* status codes */
