@@ -28,21 +28,41 @@ def _host(seed, R):
     return [[WG.normal(WG.seed_of(5, r, v, seed), n).numpy() for v, n in enumerate(NUMELS)] for r in range(R)]
 
 
-@pytest.mark.parametrize("mode", [D.MODE_FUSED, D.MODE_STAGED])
+def _oracle(host, R, cap, view, order):
+    """The oracle's gradients after one sync of ``host`` (bucket views when
+    ``view``: its gradients are views of its flat buckets)."""
+    orc = OR.Reducer(NUMELS, R, cap, gradient_as_bucket_view=view)
+    if view:
+        og = orc.views()
+        for r in range(R):
+            for v in range(len(NUMELS)):
+                og[r][v][...] = host[r][v]
+    else:
+        og = [[h.copy() for h in row] for row in host]
+        orc.bind(og)
+    orc.sync(order)
+    return og
+
+
+@pytest.mark.parametrize("mode", [D.MODE_FUSED, D.MODE_STAGED, "view"])
 def test_captured_sync_replays_match_the_oracle(mode):
     R, cap = 4, 4 * 15000
+    view = mode == "view"
     say(f"graph capture mode={mode}")
     order = WG.permutation(17, len(NUMELS))          # parked buckets included
     host = _host(1, R)
-    grads = [[torch.from_numpy(h).cuda() for h in row] for row in host]
     compute = torch.cuda.Stream()
     sides = [torch.cuda.Stream(), torch.cuda.Stream()]
     red = D.Reducer([(n,) for n in NUMELS], R, cap)
-    red.bind(grads, compute_stream=compute, side_streams=sides, mode=mode)
-    orc = OR.Reducer(NUMELS, R, cap)
-    og = [[h.copy() for h in row] for row in host]
-    orc.bind(og)
-    orc.sync(order)
+    if view:
+        grads = [[g.view(-1) for g in row] for row in red.bind_bucket_views(compute_stream=compute,
+                                                                              side_streams=sides)]
+        fill_from_host(grads, host)
+    else:
+        grads = [[torch.from_numpy(h).cuda() for h in row] for row in host]
+        red.bind(grads, compute_stream=compute, side_streams=sides, mode=mode)
+    og = _oracle(host, R, cap, view, order)
+    torch.cuda.synchronize()
     with torch.cuda.stream(compute):
         red.sync(order)                              # one eager iteration first
     torch.cuda.synchronize()
@@ -66,10 +86,7 @@ def test_captured_sync_replays_match_the_oracle(mode):
     with torch.cuda.stream(compute):
         red.sync(order)
     got = snapshot(grads)
-    og2 = [[h.copy() for h in row] for row in host2]
-    orc2 = OR.Reducer(NUMELS, R, cap)
-    orc2.bind(og2)
-    orc2.sync(order)
+    og2 = _oracle(host2, R, cap, view, order)
     for v in range(len(NUMELS)):
         for r in range(R):
             assert_bits_equal(got[v][r], og2[r][v], f"eager after replays v={v} r={r}")
