@@ -460,6 +460,42 @@ def test_workgroups_per_cu_parity(R, wg, flags, mode):
     red.close()
 
 
+def test_two_handles_interleaved_on_shared_streams():
+    """Two reducers (different shapes, replica counts, modes) bound at once,
+    sharing the compute and side streams, hooks interleaved: each must match
+    its own oracle, so no state is shared between handles."""
+    compute = torch.cuda.Stream()
+    sides = [torch.cuda.Stream(), torch.cuda.Stream()]
+    specs = [(RAGGED, 3, 4 * 9000, D.MODE_FUSED), ([70000, 5, 8192, 131072, 1], 8, 4 * 40000, D.MODE_STAGED)]
+    reds, grads, wants, orders = [], [], [], []
+    for k, (numels, R, cap, mode) in enumerate(specs):
+        say(f"handle {k}: P={len(numels)} R={R} mode={mode}")
+        red = D.Reducer([(n,) for n in numels], R, cap)
+        g = alloc_grads(numels, R)
+        red.bind(g, compute_stream=compute, side_streams=sides, mode=mode)
+        host = _host_inputs(90 + k, numels, R)
+        fill_from_host(g, host)
+        order = WG.permutation(91 + k, len(numels))
+        want, _ = _oracle_sync(numels, R, cap, host, order)
+        reds.append(red); grads.append(g); wants.append(want); orders.append(order)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(compute):
+        n = max(len(o) for o in orders)
+        for i in range(n):                           # hooks of the two models interleaved
+            for red, order in zip(reds, orders):
+                if i < len(order):
+                    red.mark_ready(order[i])
+        for red in reds:
+            red.finalize()
+    for k, (numels, R, _, _) in enumerate(specs):
+        got = snapshot(grads[k])
+        for v in range(len(numels)):
+            for r in range(R):
+                assert_bits_equal(got[v][r], wants[k][r][v], f"handle {k} v={v} r={r}")
+    for red in reds:
+        red.close()
+
+
 def _mlp_backward(params, g0, X, H, W1, W2, dY0, hook):
     """Backward of [Linear(d, f), Linear(f, d)] blocks in bf16, last layer
     first; fp32 gradients of replica 0 are written in place."""
