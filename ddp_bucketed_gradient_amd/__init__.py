@@ -29,8 +29,9 @@ def _fwd(name):
 for _n in ["reducer_create", "destroy", "num_buckets", "get_locator", "get_bucket", "num_segments",
            "get_bucket_segments", "get_segment", "workspace_bytes", "bind", "ensure_prior_reduction_finished",
            "mark_ready", "mark_ready_many", "finalize", "set_sync", "no_sync_accumulate", "reset",
-           "get_launch_log", "get_launch_times", "device_clock_hz", "last_error", "set_launch_blocks", "set_workgroups_per_cu",
+           "get_launch_log", "get_launch_times", "device_clock_hz", "last_error", "set_launch_blocks",
+           "set_workgroups_per_cu",
            "view_storage_elems", "get_view_offset", "bind_bucket_views", "rebuild_buckets", "get_ready_order",
-           "set_local_used"]:
+           "set_local_used", "set_sync_step"]:
     globals()[_n] = _fwd(_n)
 del _n

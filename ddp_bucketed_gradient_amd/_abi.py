@@ -29,7 +29,7 @@ SYMBOLS = [
     "ddpb_bind", "ddpb_ensure_prior_reduction_finished", "ddpb_mark_ready", "ddpb_mark_ready_many",
     "ddpb_finalize", "ddpb_set_sync", "ddpb_no_sync_accumulate", "ddpb_reset", "ddpb_get_launch_log",
     "ddpb_get_launch_times", "ddpb_device_clock_hz", "ddpb_last_error", "ddpb_set_launch_blocks",
-    "ddpb_set_workgroups_per_cu",
+    "ddpb_set_workgroups_per_cu", "ddpb_set_sync_step",
     "ddpb_view_storage_elems", "ddpb_get_view_offset", "ddpb_bind_bucket_views",
     "ddpb_rebuild_buckets", "ddpb_get_ready_order", "ddpb_set_local_used",
 ]
@@ -63,6 +63,7 @@ def _sig(lib):
         "ddpb_finalize": [vp],
         "ddpb_set_sync": [vp, i32],
         "ddpb_no_sync_accumulate": [vp, C.POINTER(vp), i32, i32],
+        "ddpb_set_sync_step": [vp, C.POINTER(vp), i32, i32],
         "ddpb_reset": [vp],
         "ddpb_get_launch_log": [vp, P32, P32, P64, P64, i32, P32],
         "ddpb_get_launch_times": [vp, i32, C.POINTER(C.c_float), C.POINTER(C.c_float), i32, P32],
@@ -184,6 +185,10 @@ class Lib:
     def no_sync_accumulate(self, h, step_ptrs: Sequence[int], step_dtype: int, first_step: bool):
         sp = (vp * max(len(step_ptrs), 1))(*[vp(int(p)) if p else vp() for p in step_ptrs])
         self._check(self.dll.ddpb_no_sync_accumulate(h, sp, step_dtype, 1 if first_step else 0))
+
+    def set_sync_step(self, h, step_ptrs: Sequence[int], step_dtype: int, first_step: bool):
+        sp = (vp * max(len(step_ptrs), 1))(*[vp(int(p)) if p else vp() for p in step_ptrs])
+        self._check(self.dll.ddpb_set_sync_step(h, sp, step_dtype, 1 if first_step else 0))
 
     def reset(self, h):
         self._check(self.dll.ddpb_reset(h))

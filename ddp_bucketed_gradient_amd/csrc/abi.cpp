@@ -316,6 +316,12 @@ int ddpb_set_launch_blocks(ddpb_t h, int32_t max_blocks) {
   return DDPB_OK;
 }
 
+int ddpb_set_sync_step(ddpb_t h, void* const* step_ptrs, int32_t step_dtype, int32_t first_step) {
+  if (!h) return fail(DDPB_E_ARG, "set_sync_step: NULL handle");
+  std::string err;
+  return pass(h->red.set_sync_step(step_ptrs, step_dtype, first_step != 0, &err), err);
+}
+
 int ddpb_set_workgroups_per_cu(ddpb_t h, int32_t n) {
   if (!h || n < 0 || n > 2) return fail(DDPB_E_ARG, "set_workgroups_per_cu: n must be 0, 1 or 2");
   std::string err;

@@ -42,6 +42,7 @@ int Reducer::bind(const BindArgs& args, std::string* err) {
     rc = launcher_->bind(plan_, args, err);
   }
   bound_ = (rc == kOk);
+  sync_step_set_ = false;          // the launcher's tables were released
   // The launch log and the timing history refer to the previous binding's
   // buckets and events: start both afresh.
   log_.clear();
@@ -147,6 +148,35 @@ int Reducer::set_local_used(const uint8_t* used, std::string* err) {
   return kOk;
 }
 
+int Reducer::set_sync_step(void* const* step_ptrs, int32_t step_dtype, bool first, std::string* err) {
+  if (!bound_) {
+    *err = "set_sync_step: reducer is not bound";
+    return kErrState;
+  }
+  if (step_ptrs == nullptr || (step_dtype != 0 && step_dtype != 1)) {
+    *err = "set_sync_step: bad step pointers or dtype";
+    return kErrArg;
+  }
+  if (iteration_open()) {
+    *err = "set_sync_step: must come before the iteration's hooks";
+    return kErrState;
+  }
+  if (!sync_) {
+    *err = "set_sync_step: synchronisation is off; accumulate no_sync steps with ddpb_no_sync_accumulate";
+    return kErrState;
+  }
+  const int rc = launcher_->set_sync_step(step_ptrs, step_dtype, first, err);
+  if (rc == kOk) sync_step_set_ = true;
+  return rc;
+}
+
+void Reducer::drop_sync_step() {
+  if (!sync_step_set_) return;
+  sync_step_set_ = false;
+  std::string e2;
+  launcher_->set_sync_step(nullptr, 0, false, &e2);
+}
+
 int Reducer::finalize(std::string* err) {
   if (!bound_) {
     *err = "finalize: reducer is not bound";
@@ -181,6 +211,7 @@ int Reducer::finalize(std::string* err) {
     std::string e2;
     launcher_->set_used(nullptr, nullptr, &e2);
   }
+  drop_sync_step();                       // ... and so did the step
   ++finalized_;
   begin_iteration();
   return rc;
@@ -189,6 +220,10 @@ int Reducer::finalize(std::string* err) {
 int Reducer::set_sync(bool enabled, std::string* err) {
   if (iteration_open()) {
     *err = "set_sync: an iteration is in progress";
+    return kErrState;
+  }
+  if (!enabled && sync_step_set_) {
+    *err = "set_sync: a step is set for the coming synchronisation (ddpb_set_sync_step)";
     return kErrState;
   }
   sync_ = enabled;
@@ -223,6 +258,7 @@ int Reducer::rebuild_buckets(int64_t cap_bytes, std::string* err) {
   const std::vector<int32_t> order = last_order_;
   plan_ = make_plan(plan_.numel, plan_.elem_size, cap_bytes, plan_.R, &order);
   bound_ = false;                  // device tables and events follow the new plan at the next bind
+  drop_sync_step();
   log_.clear();
   begin_iteration();
   return kOk;
@@ -230,6 +266,7 @@ int Reducer::rebuild_buckets(int64_t cap_bytes, std::string* err) {
 
 int Reducer::reset() {
   failed_ = false;
+  drop_sync_step();
   begin_iteration();
   return kOk;
 }

@@ -137,6 +137,9 @@ class Launcher {
   // over replicas per variable), or NULL for "all used". Ordered on the
   // compute stream before the next launch's ready event.
   virtual int set_used(const uint8_t* used, const uint8_t* global, std::string* err) = 0;
+  // Step gradients (R * P, replica-major) that the coming synchronisation adds
+  // to every replica's gradient as it reduces each bucket, or NULL for none.
+  virtual int set_sync_step(void* const* step_ptrs, int32_t step_dtype, bool first, std::string* err) = 0;
 };
 
 std::unique_ptr<Launcher> make_launcher();
@@ -161,6 +164,9 @@ class Reducer {
   // Per-replica used flags (R * P, replica-major; NULL = all used) for the
   // coming synchronisation; OR-ed with earlier calls since the last sync.
   int set_local_used(const uint8_t* used, std::string* err);
+  // [Li] "Gradient Accumulation (no_sync)": the last local step of a no_sync
+  // run, accumulated by the coming synchronisation itself, bucket by bucket.
+  int set_sync_step(void* const* step_ptrs, int32_t step_dtype, bool first, std::string* err);
   const std::vector<int32_t>& last_ready_order() const { return last_order_; }
   const std::vector<LaunchRecord>& log() const { return log_; }
   int64_t finalized() const { return finalized_; }
@@ -191,6 +197,9 @@ class Reducer {
   bool has_order_ = false;
   std::vector<uint8_t> used_acc_;    // R * P used flags, OR-ed until the next sync
   bool used_set_ = false;
+  bool sync_step_set_ = false;       // a step for the coming synchronisation is set
+
+  void drop_sync_step();
 
   int launch_ready(int32_t call, std::string* err);
   int mark_unused_ready(int32_t call, std::string* err);

@@ -659,6 +659,133 @@ __global__ __launch_bounds__(kBlock) void accumulate_kernel(const Segment* __res
 }
 
 
+// The synchronising micro-step fused into the reduction ([Li] "Gradient
+// Accumulation (no_sync)": the last local backward accumulates into the
+// gradients, then the buckets are averaged). Each replica's gradient enters
+// the mean as accumulate_kernel would leave it -- float(step) on a first
+// step, grad + float(step) otherwise, grad itself where the replica has no
+// step (NULL; +0.0 on a first step) -- summed in replica order and divided
+// once; the mean is written back. One HBM pass instead of an accumulation
+// pass and a reduction pass. Replica count at run time, replicas in chunks of
+// kRtChunk as in fused_mean_kernel_rt.
+template <bool BF16, bool FIRST>
+__device__ __forceinline__ v4f acc_step4(const float* acc, const void* step, int64_t e) {
+  v4f x = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (!FIRST) x = ld4s(acc + e);
+  if (step == nullptr) return x;
+  v4f s4;
+  if (BF16) {
+    const v2u b = __builtin_nontemporal_load((const gv2u*)(static_cast<const uint16_t*>(step) + e));
+    s4.x = __uint_as_float(b.x << 16);
+    s4.y = __uint_as_float(b.x & 0xffff0000u);
+    s4.z = __uint_as_float(b.y << 16);
+    s4.w = __uint_as_float(b.y & 0xffff0000u);
+  } else {
+    s4 = ld4s(static_cast<const float*>(step) + e);
+  }
+  if (FIRST) return s4;
+  x.x = x.x + s4.x;
+  x.y = x.y + s4.y;
+  x.z = x.z + s4.z;
+  x.w = x.w + s4.w;
+  return x;
+}
+
+template <bool BF16, bool FIRST>
+__device__ __forceinline__ float acc_step1(const float* acc, const void* step, int64_t e) {
+  const float a = FIRST ? 0.0f : G(acc)[e];
+  if (step == nullptr) return a;
+  const float s1 = BF16 ? bf16_to_f32(((const __attribute__((address_space(1))) uint16_t*)step)[e])
+                        : ((const gfloat*)step)[e];
+  return FIRST ? s1 : a + s1;
+}
+
+template <bool BF16, bool FIRST>
+__global__ __launch_bounds__(kBlock) void fused_acc_mean_kernel(const Segment* __restrict__ segs, int32_t nseg,
+                                                                float* const* __restrict__ grads,
+                                                                const void* const* __restrict__ steps, int32_t P,
+                                                                int32_t R, float scale, int32_t pow2, int32_t vec_ok,
+                                                                int64_t* __restrict__ stamp) {
+  stamp_begin(stamp);
+  // One wavefront per segment; with a capped grid (fewer workgroups than
+  // segments / 4) each wavefront strides over the remaining segments.
+  for (int s = blockIdx.x * kWavesPerBlock + wave_id(); s < nseg; s += gridDim.x * kWavesPerBlock) {
+    const Segment g = segs[s];
+    const int len = static_cast<int>(g.len);
+    const int lane = lane_id();
+    int tail = 0;
+    if (vec_ok && (g.flags & kSegVecStart)) {
+      uintptr_t any = 0, anys = 0;           // alignment of every gradient (16 B) and step (8 / 16 B)
+      for (int r = 0; r < R; ++r) {
+        const int64_t k = static_cast<int64_t>(r) * P + g.var;
+        any |= reinterpret_cast<uintptr_t>(grads[k] + g.start);
+        if (steps[k] != nullptr)
+          anys |= reinterpret_cast<uintptr_t>(steps[k]) + static_cast<uintptr_t>(g.start) * (BF16 ? 2 : 4);
+      }
+      if ((any & 15) == 0 && (anys & (BF16 ? 7 : 15)) == 0) {
+        const int n4 = len >> 2;
+        for (int i = lane; i < n4; i += 64 * kRtU) {
+          v4f a[kRtU];
+          for (int r0 = 0; r0 < R; r0 += kRtChunk) {
+            v4f x[kRtU][kRtChunk];
+#pragma unroll
+            for (int u = 0; u < kRtU; ++u)
+#pragma unroll
+              for (int q = 0; q < kRtChunk; ++q)
+                if (r0 + q < R && i + 64 * u < n4) {
+                  const int64_t k = static_cast<int64_t>(r0 + q) * P + g.var;
+                  x[u][q] = acc_step4<BF16, FIRST>(grads[k], steps[k], g.start + 4 * (i + 64 * u));
+                }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < kRtU; ++u) {
+              if (i + 64 * u < n4) {
+#pragma unroll
+                for (int q = 0; q < kRtChunk; ++q) {
+                  if (r0 + q < R) {
+                    if (r0 + q == 0) {
+                      a[u] = x[u][q];
+                    } else {
+                      a[u].x = a[u].x + x[u][q].x;
+                      a[u].y = a[u].y + x[u][q].y;
+                      a[u].z = a[u].z + x[u][q].z;
+                      a[u].w = a[u].w + x[u][q].w;
+                    }
+                  }
+                }
+              }
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < kRtU; ++u) {
+            if (i + 64 * u < n4) {
+              v4f m;
+              m.x = finish_rt(a[u].x, R, scale, pow2 != 0);
+              m.y = finish_rt(a[u].y, R, scale, pow2 != 0);
+              m.z = finish_rt(a[u].z, R, scale, pow2 != 0);
+              m.w = finish_rt(a[u].w, R, scale, pow2 != 0);
+              for (int r = 0; r < R; ++r)
+                st4s(grads[static_cast<int64_t>(r) * P + g.var] + g.start + 4 * (i + 64 * u), m);
+            }
+          }
+        }
+        tail = n4 * 4;
+      }
+    }
+    // scalar path: ragged tails and unaligned pointers
+    for (int j = tail + lane; j < len; j += 64) {
+      float a = acc_step1<BF16, FIRST>(grads[g.var], steps[g.var], g.start + j);
+      for (int r = 1; r < R; ++r) {
+        const int64_t k = static_cast<int64_t>(r) * P + g.var;
+        a = a + acc_step1<BF16, FIRST>(grads[k], steps[k], g.start + j);
+      }
+      const float m = finish_rt(a, R, scale, pow2 != 0);
+      for (int r = 0; r < R; ++r) G(grads[static_cast<int64_t>(r) * P + g.var])[g.start + j] = m;
+    }
+  }
+  stamp_end(stamp);
+}
+
 // ---------------------------------------------------------------------------
 // launcher
 
@@ -714,6 +841,12 @@ class HipLauncher final : public Launcher {
     HIP_OK(hipHostMalloc(&h_steps_, std::max<size_t>(nptr, 1) * kStepSlots * sizeof(void*), hipHostMallocDefault),
            "hipHostMalloc(step staging)");
     HIP_OK(hipMalloc(&d_used_, std::max<size_t>(nptr, 1)), "hipMalloc(used flags)");
+    HIP_OK(hipMalloc(&d_sync_steps_, std::max<size_t>(nptr, 1) * sizeof(void*)), "hipMalloc(sync step table)");
+    HIP_OK(hipHostMalloc(&h_sync_steps_, std::max<size_t>(nptr, 1) * sizeof(void*), hipHostMallocDefault),
+           "hipHostMalloc(sync step staging)");
+    HIP_OK(hipEventCreateWithFlags(&ev_sync_steps_, hipEventDisableTiming), "hipEventCreate");
+    sync_steps_recorded_ = false;
+    sync_step_active_ = false;
     HIP_OK(hipHostMalloc(&h_used_, std::max<size_t>(nptr, 1), hipHostMallocDefault), "hipHostMalloc(used staging)");
     HIP_OK(hipEventCreateWithFlags(&ev_used_, hipEventDisableTiming), "hipEventCreate");
     used_recorded_ = false;
@@ -839,18 +972,18 @@ class HipLauncher final : public Launcher {
     const void* const* tab = d_steps_ + slot * nptr;
     if (step_dtype == 1) {
       if (first)
-        hipLaunchKernelGGL((accumulate_kernel<true, true>), grid, dim3(kBlock), lds_one_per_cu_, compute_, d_segs_, nseg,
-                           d_grads_, tab, P_, R_, vec);
+        hipLaunchKernelGGL((accumulate_kernel<true, true>), grid, dim3(kBlock), lds_one_per_cu_, compute_, d_segs_,
+                           nseg, d_grads_, tab, P_, R_, vec);
       else
-        hipLaunchKernelGGL((accumulate_kernel<true, false>), grid, dim3(kBlock), lds_one_per_cu_, compute_, d_segs_, nseg,
-                           d_grads_, tab, P_, R_, vec);
+        hipLaunchKernelGGL((accumulate_kernel<true, false>), grid, dim3(kBlock), lds_one_per_cu_, compute_, d_segs_,
+                           nseg, d_grads_, tab, P_, R_, vec);
     } else {
       if (first)
-        hipLaunchKernelGGL((accumulate_kernel<false, true>), grid, dim3(kBlock), lds_one_per_cu_, compute_, d_segs_, nseg,
-                           d_grads_, tab, P_, R_, vec);
+        hipLaunchKernelGGL((accumulate_kernel<false, true>), grid, dim3(kBlock), lds_one_per_cu_, compute_, d_segs_,
+                           nseg, d_grads_, tab, P_, R_, vec);
       else
-        hipLaunchKernelGGL((accumulate_kernel<false, false>), grid, dim3(kBlock), lds_one_per_cu_, compute_, d_segs_, nseg,
-                           d_grads_, tab, P_, R_, vec);
+        hipLaunchKernelGGL((accumulate_kernel<false, false>), grid, dim3(kBlock), lds_one_per_cu_, compute_, d_segs_,
+                           nseg, d_grads_, tab, P_, R_, vec);
     }
     HIP_OK(hipGetLastError(), "launch accumulate_kernel");
     return kOk;
@@ -921,6 +1054,32 @@ class HipLauncher final : public Launcher {
     return kOk;
   }
 
+  int set_sync_step(void* const* step_ptrs, int32_t step_dtype, bool first, std::string* err) override {
+    if (step_ptrs == nullptr) {
+      sync_step_active_ = false;
+      return kOk;
+    }
+    const size_t n = static_cast<size_t>(R_) * P_;
+    bool cap = false;
+    if (const int rc = capturing(compute_, &cap, err); rc != kOk) return rc;
+    if (cap) {                     // the table comes from host staging that later calls reuse
+      *err = "ddpb_set_sync_step cannot be captured into a graph";
+      return kErrState;
+    }
+    // The staging buffer may still feed the previous upload.
+    if (sync_steps_recorded_) HIP_OK(hipEventSynchronize(ev_sync_steps_), "hipEventSynchronize(sync step)");
+    std::memcpy(h_sync_steps_, step_ptrs, n * sizeof(void*));
+    if (n)
+      HIP_OK(hipMemcpyAsync(d_sync_steps_, h_sync_steps_, n * sizeof(void*), hipMemcpyHostToDevice, compute_),
+             "upload sync step table");
+    HIP_OK(hipEventRecord(ev_sync_steps_, compute_), "hipEventRecord(sync step)");
+    sync_steps_recorded_ = true;
+    sync_step_active_ = true;
+    sync_step_bf16_ = (step_dtype == 1);
+    sync_step_first_ = first;
+    return kOk;
+  }
+
   int clock_hz(int64_t* hz, std::string* err) override {
     int dev = 0, khz = 0;
     HIP_OK(hipGetDevice(&dev), "hipGetDevice");
@@ -945,6 +1104,44 @@ class HipLauncher final : public Launcher {
       if (t0) HIP_OK(hipEventRecord(t0, s), "hipEventRecord(t0)");
       if (t1) HIP_OK(hipEventRecord(t1, s), "hipEventRecord(t1)");
       return kOk;
+    }
+    if (sync_step_active_) {
+      // the synchronising micro-step: per-variable segments, steps per variable
+      const int32_t v0 = plan_->seg_first[b];
+      const int32_t vn = plan_->seg_first[b + 1] - v0;
+      int64_t vblocks = (vn + kWavesPerBlock - 1) / kWavesPerBlock;
+      if (max_blocks_ > 0) vblocks = std::min<int64_t>(vblocks, max_blocks_);
+      const dim3 vgrid(static_cast<unsigned>(vblocks));
+      const void* const* steps = d_sync_steps_;
+      if ((mode_ == kModeFused || mode_ == kModeBucketView) && !used_active_) {
+        const int32_t p2 = pow2_ ? 1 : 0;
+        int64_t* st = (flags_ & 1) ? d_stamps_ + static_cast<int64_t>(b) * 4 : nullptr;
+#define DDPB_ACC_MEAN(BF, FI)                                                                                   \
+  hipExtLaunchKernelGGL((fused_acc_mean_kernel<BF, FI>), vgrid, dim3(kBlock), lds_reserve_, s, t0, t1, 0,       \
+                        d_segs_ + v0, vn, d_grads_, steps, P_, R_, scale_, p2, vec_ok_, st)
+        if (sync_step_bf16_) {
+          if (sync_step_first_) DDPB_ACC_MEAN(true, true); else DDPB_ACC_MEAN(true, false);
+        } else {
+          if (sync_step_first_) DDPB_ACC_MEAN(false, true); else DDPB_ACC_MEAN(false, false);
+        }
+#undef DDPB_ACC_MEAN
+        HIP_OK(hipGetLastError(), "launch fused_acc_mean_kernel");
+        return kOk;
+      }
+      // staged mode or used flags: accumulate the bucket's variables first,
+      // on this side stream, then reduce as usual
+      const dim3 agrid(static_cast<unsigned>((static_cast<int64_t>(vn) * R_ + kWavesPerBlock - 1) / kWavesPerBlock));
+#define DDPB_ACC(BF, FI)                                                                                         \
+  hipExtLaunchKernelGGL((accumulate_kernel<BF, FI>), agrid, dim3(kBlock), lds_one_per_cu_, s, t0, nullptr, 0,  \
+                        d_segs_ + v0, vn, d_grads_, steps, P_, R_, vec_ok_)
+      if (sync_step_bf16_) {
+        if (sync_step_first_) DDPB_ACC(true, true); else DDPB_ACC(true, false);
+      } else {
+        if (sync_step_first_) DDPB_ACC(false, true); else DDPB_ACC(false, false);
+      }
+#undef DDPB_ACC
+      HIP_OK(hipGetLastError(), "launch accumulate_kernel");
+      t0 = nullptr;                            // the bucket's start is the accumulation's
     }
     const Segment* segs = (view ? d_view_segs_ : d_segs_) + s0;
     float* const* table = view ? d_view_bases_ : d_grads_;
@@ -1058,6 +1255,14 @@ class HipLauncher final : public Launcher {
     d_view_segs_ = nullptr;
     if (h_steps_) (void)hipHostFree(h_steps_);
     if (ev_used_) (void)hipEventDestroy(ev_used_);
+    if (ev_sync_steps_) (void)hipEventDestroy(ev_sync_steps_);
+    if (d_sync_steps_) (void)hipFree(d_sync_steps_);
+    if (h_sync_steps_) (void)hipHostFree(h_sync_steps_);
+    ev_sync_steps_ = nullptr;
+    d_sync_steps_ = nullptr;
+    h_sync_steps_ = nullptr;
+    sync_step_active_ = false;
+    sync_steps_recorded_ = false;
     if (d_used_) (void)hipFree(d_used_);
     if (h_used_) (void)hipHostFree(h_used_);
     ev_used_ = nullptr;
@@ -1097,6 +1302,13 @@ class HipLauncher final : public Launcher {
   hipEvent_t ev_used_ = nullptr;
   bool used_recorded_ = false;
   bool used_active_ = false;
+  void** d_sync_steps_ = nullptr;   // R x P step pointers of the synchronising micro-step
+  void** h_sync_steps_ = nullptr;   // pinned staging for their upload
+  hipEvent_t ev_sync_steps_ = nullptr;
+  bool sync_steps_recorded_ = false;
+  bool sync_step_active_ = false;
+  bool sync_step_bf16_ = false;
+  bool sync_step_first_ = false;
   float* flat_ = nullptr;
   float* avg_ = nullptr;
   std::vector<hipEvent_t> ev_ready_, ev_done_, ev_slot_, ev_t0_, ev_t1_;

@@ -27,6 +27,7 @@ class NullLauncher final : public Launcher {
   void set_max_blocks(int32_t) override {}
   int set_workgroups_per_cu(int32_t, std::string*) override { return kOk; }
   int set_used(const uint8_t*, const uint8_t*, std::string*) override { return kOk; }
+  int set_sync_step(void* const*, int32_t, bool, std::string*) override { return kOk; }
   int clock_hz(int64_t* hz, std::string*) override {
     *hz = 0;
     return kOk;

@@ -159,6 +159,20 @@ class Reducer:
         """steps[r][v]: contiguous fp32 or bf16 CUDA tensor per replica/variable,
         or None where that replica produced no gradient (zeros on the first
         step, unchanged afterwards)."""
+        ptrs, code = self._step_table(steps)
+        self.lib.no_sync_accumulate(self.h, ptrs, code, first_step)
+
+    def set_sync_step(self, steps, first_step: bool = False):
+        """The last local step of a no_sync run, added to the gradients by the
+        coming synchronisation itself (set before its first hook; the same
+        result as no_sync_accumulate followed by the sync, in one pass).
+        ``steps`` as for no_sync_accumulate; the tensors must stay alive until
+        finalize."""
+        ptrs, code = self._step_table(steps)
+        self.lib.set_sync_step(self.h, ptrs, code, first_step)
+        self._keep_steps = steps
+
+    def _step_table(self, steps):
         import torch
         present = [t for row in steps for t in row if t is not None]
         dt = present[0].dtype if present else torch.float32
@@ -177,7 +191,7 @@ class Reducer:
                 if t.numel() != self._numel[v]:
                     raise ValueError(f"steps[{r}][{v}] has {t.numel()} elements, the variable {self._numel[v]}")
                 ptrs.append(t.data_ptr())
-        self.lib.no_sync_accumulate(self.h, ptrs, code, first_step)
+        return ptrs, code
 
     def set_local_used(self, used):
         """Which replicas use which variables in the coming backward pass: an

@@ -267,6 +267,28 @@ int ddpb_set_sync(ddpb_t h, int32_t enabled);
 int ddpb_no_sync_accumulate(ddpb_t h, void* const* step_ptrs, int32_t step_dtype,
                             int32_t first_step);
 
+/* The last local step of a no_sync run, accumulated by the synchronisation
+ * itself ([Li] "Gradient Accumulation (no_sync)": the backward that leaves
+ * no_sync adds its gradients to the accumulated ones, then the buckets are
+ * averaged). Instead of calling ddpb_no_sync_accumulate and then firing the
+ * hooks, the caller sets the step here and fires the hooks as its gradients
+ * become final: each bucket's reduction then forms, per replica and element,
+ * exactly what ddpb_no_sync_accumulate(step_ptrs, step_dtype, first_step)
+ * would leave in the gradient and averages that -- the same bits in one pass
+ * over HBM instead of two. The step table is uploaded now (on the compute
+ * stream); the step memory is read when each bucket is reduced, so it must
+ * stay valid until ddpb_finalize.
+ *   step_ptrs, step_dtype, first_step   as for ddpb_no_sync_accumulate
+ * Must come before the iteration's first ddpb_mark_ready, with sync enabled
+ * (else DDPB_E_STATE); consumed by that iteration's ddpb_finalize, dropped by
+ * ddpb_reset, a rebind or a rebuild. While it is set, ddpb_set_sync(h, 0) is
+ * refused. Fused and bucket-view modes reduce each bucket in one kernel; in
+ * staged mode, or with used flags, each bucket's variables are accumulated
+ * on its side stream just before its reduction. Refused during graph capture
+ * (the table comes from host staging). */
+int ddpb_set_sync_step(ddpb_t h, void* const* step_ptrs, int32_t step_dtype,
+                       int32_t first_step);
+
 /* Unused parameters ([Li] "Handling Unused Parameters and Sub-Graph
  * Execution"; [TP] "When a parameter never receives a gradient"; [C30]
  * "Unused Parameter"): which replicas will produce a gradient for which

@@ -150,6 +150,39 @@ def test_plan_of_a_tensor_beyond_int32_elements(host):
         assert host.view_storage_elems(red.h) == flat
 
 
+def test_sync_step_rules(host):
+    """ddpb_set_sync_step: bound, before the iteration's hooks, with sync on;
+    consumed by finalize, dropped by reset; sync cannot be turned off while
+    it is set."""
+    red = _reducer(host, [10, 20], 2, 0)
+    fake = [0x2000 + 16 * i for i in range(4)]
+
+    def code(fn):
+        with pytest.raises(D.DdpbError) as e:
+            fn()
+        return e.value.code
+
+    assert code(lambda: host.set_sync_step(red.h, fake, D.BF16, False)) == D.E_STATE      # not bound
+    _bind_fake(red)
+    assert code(lambda: host.set_sync_step(red.h, fake, 7, False)) == D.E_ARG             # bad dtype
+    host.set_sync_step(red.h, fake, D.BF16, False)
+    assert code(lambda: red.set_sync(False)) == D.E_STATE                                 # step pending
+    red.mark_ready(1)
+    assert code(lambda: host.set_sync_step(red.h, fake, D.BF16, False)) == D.E_STATE      # iteration open
+    red.mark_ready(0)
+    red.finalize()
+    red.set_sync(False)                                                                   # consumed
+    assert code(lambda: host.set_sync_step(red.h, fake, D.F32, True)) == D.E_STATE        # sync off
+    red.set_sync(True)
+    host.set_sync_step(red.h, fake, D.F32, True)
+    red.reset()
+    red.set_sync(False)                                                                   # dropped by reset
+    red.set_sync(True)
+    host.set_sync_step(red.h, fake, D.F32, False)
+    _bind_fake(red)
+    red.set_sync(False)                                                                   # dropped by a rebind
+
+
 def test_workgroups_per_cu_arguments(host):
     red = _reducer(host, [10, 20], 2, 0)
     for n in (0, 1, 2):
