@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--launch-blocks", type=int, default=None,
                     help="cap on workgroups per reduction launch (0 = whole GPU); "
                          "default 0, and for --config 5 a sweep")
+    ap.add_argument("--fused-last-step", action="store_true",
+                    help="--config 4: the synchronising micro-step is accumulated by the reduction "
+                         "itself (ddpb_set_sync_step) instead of a separate accumulation pass")
     ap.add_argument("--wg-per-cu", type=int, default=None, choices=[0, 1, 2],
                     help="reduction workgroups per compute unit (0 = no limit); default the "
                          "library's (1), and for --config 5 a sweep of 1 and 0")
@@ -464,6 +467,10 @@ def run_nosync_bench(args, torch, D, WG, WC):
         for t in range(k):
             if t == k - 1:
                 red.set_sync(True)
+                if args.fused_last_step:       # the sync accumulates this step itself
+                    red.set_sync_step(steps[t], first_step=(t == 0))
+                    red.sync(order)
+                    continue
             e0 = e1 = None
             if timed:
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -490,7 +497,9 @@ def run_nosync_bench(args, torch, D, WG, WC):
     # the time the reduction occupied the GPU
     st, ds = red.launch_times_ms(0, True)
     sync_ms = union_length(st, ds)
-    alg = R * N * (6 + 10 * (k - 1)) + 2 * R * S
+    # accumulation bytes of every micro-step, plus the sync's read and write of
+    # every replica -- which the fused last step folds into its accumulation
+    alg = R * N * (6 + 10 * (k - 1)) + (0 if args.fused_last_step else 2 * R * S)
     value = alg / (wall_ms * 1e-3) / 1e9
     avg_rest = sum(acc_rest) / len(acc_rest)
     bytes_rest = 10 * R * N
@@ -502,11 +511,13 @@ def run_nosync_bench(args, torch, D, WG, WC):
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "tensors": P, "params": N, "replicas": R, "micro_steps": k,
                    "step_dtype": "bf16", "buckets": red.num_buckets, "workgroups_per_cu": wg_per_cu,
+                   "fused_last_step": args.fused_last_step,
                    "alg_bytes_per_step": alg},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "accumulate_first_ms": round(sum(acc_first) / len(acc_first), 4),
         "accumulate_ms": round(avg_rest, 4), "sync_busy_ms_last": round(sync_ms, 4),
-        "sync_busy_GBps_last": round(2 * R * S / (sync_ms * 1e-3) / 1e9, 1),
+        # the fused last step reads the accumulators and the bf16 steps and writes the mean
+        "sync_busy_GBps_last": round((10 * R * N if args.fused_last_step else 2 * R * S) / (sync_ms * 1e-3) / 1e9, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic_from_profiles("accumulate_kernel<bf16,add>", w.name),

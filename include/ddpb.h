@@ -190,7 +190,8 @@ int ddpb_bind_bucket_views(ddpb_t h, void* const* replica_storage, int64_t stora
 int ddpb_set_launch_blocks(ddpb_t h, int32_t max_blocks);
 
 /* At most n workgroups of the reduction kernels (fused, bucket-view and staged
- * modes) share one compute unit, counting every launch in flight: n = 1 (the
+ * modes; not the kernel that also accumulates a ddpb_set_sync_step step,
+ * which runs without a limit) share one compute unit, counting every launch in flight: n = 1 (the
  * default) or 2, or 0 for no limit beyond the kernels' register budget (three
  * per CU for the fused kernel used without used flags). One per CU gives the
  * highest throughput for a synchronisation running alone: a CU holding two
