@@ -248,8 +248,9 @@ int ddpb_finalize(ddpb_t h);
  * graph holds every bucket kernel with its ordering. Replaying the graph
  * repeats the device work only; the host state machine advanced once, at
  * capture. Refused during capture (DDPB_E_STATE, nothing recorded):
- * ddpb_no_sync_accumulate and an iteration with ddpb_set_local_used flags
- * (both upload tables from host staging that later calls reuse), and any
+ * ddpb_no_sync_accumulate, ddpb_set_sync_step and an iteration with
+ * ddpb_set_local_used flags (all upload tables from host staging that later
+ * calls reuse), and any
  * launch of a binding made with DDPB_BIND_TIME_LAUNCHES. A refusal inside
  * ddpb_mark_ready latches DDPB_E_INCOMPLETE like any failed launch. */
 

@@ -108,6 +108,9 @@ def test_uncapturable_calls_are_refused_inside_a_capture():
         with pytest.raises(D.DdpbError) as e:
             red.no_sync_accumulate(steps, True)
         assert e.value.code == D.E_STATE
+        with pytest.raises(D.DdpbError) as e:
+            red.set_sync_step(steps, False)           # its table comes from host staging too
+        assert e.value.code == D.E_STATE
         red.sync()                                   # the capture itself stays usable
     torch.cuda.synchronize()
     g.replay()
