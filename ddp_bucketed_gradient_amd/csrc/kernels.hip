@@ -549,6 +549,11 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 // byte is touched once per micro-step; the accumulators of a large model do
 // not stay cached from one micro-step to the next).
 constexpr int kAccU = 8;
+// Synchronising step (fused_acc_mean_kernel): replicas per chunk and float4
+// groups per lane in flight. Every load of a chunk issues before its adds:
+// 16 replicas x 2 groups = 32 accumulator and 32 step loads per lane.
+constexpr int kAccMeanChunk = 16;
+constexpr int kAccMeanU = 2;
 constexpr bool kAccNT = true;
 
 template <bool NT>
@@ -667,28 +672,50 @@ __global__ __launch_bounds__(kBlock) void accumulate_kernel(const Segment* __res
 // step (NULL; +0.0 on a first step) -- summed in replica order and divided
 // once; the mean is written back. One HBM pass instead of an accumulation
 // pass and a reduction pass. Replica count at run time, replicas in chunks of
-// kRtChunk as in fused_mean_kernel_rt.
+// kAccMeanChunk.
+// The loads and the arithmetic are separate so that a group issues every
+// replica's loads before it consumes any: an add next to the loads (or a branch
+// on a NULL step between them) makes the compiler wait for each replica's loads
+// before issuing the next replica's, one round trip per replica.
+template <bool BF16>
+struct StepRaw {
+  typedef v4f T;                             // fp32 step: four floats
+};
+template <>
+struct StepRaw<true> {
+  typedef v2u T;                             // bf16 step: four bf16 in two dwords
+};
+
+template <bool BF16>
+__device__ __forceinline__ typename StepRaw<BF16>::T step_ld4(const void* step, int64_t e) {
+  if constexpr (BF16) return __builtin_nontemporal_load((const gv2u*)(static_cast<const uint16_t*>(step) + e));
+  else return ld4s(static_cast<const float*>(step) + e);
+}
+
+// What the accumulation would leave in one replica's gradient: float(step) on
+// a first step, acc + float(step) otherwise; acc where the replica has no step
+// (+0.0 on a first step).
 template <bool BF16, bool FIRST>
-__device__ __forceinline__ v4f acc_step4(const float* acc, const void* step, int64_t e) {
-  v4f x = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (!FIRST) x = ld4s(acc + e);
-  if (step == nullptr) return x;
+__device__ __forceinline__ v4f acc_combine4(v4f acc, typename StepRaw<BF16>::T raw, bool has_step) {
+  if (!has_step) {
+    if (FIRST) return v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    return acc;
+  }
   v4f s4;
-  if (BF16) {
-    const v2u b = __builtin_nontemporal_load((const gv2u*)(static_cast<const uint16_t*>(step) + e));
-    s4.x = __uint_as_float(b.x << 16);
-    s4.y = __uint_as_float(b.x & 0xffff0000u);
-    s4.z = __uint_as_float(b.y << 16);
-    s4.w = __uint_as_float(b.y & 0xffff0000u);
+  if constexpr (BF16) {
+    s4.x = __uint_as_float(raw.x << 16);
+    s4.y = __uint_as_float(raw.x & 0xffff0000u);
+    s4.z = __uint_as_float(raw.y << 16);
+    s4.w = __uint_as_float(raw.y & 0xffff0000u);
   } else {
-    s4 = ld4s(static_cast<const float*>(step) + e);
+    s4 = raw;
   }
   if (FIRST) return s4;
-  x.x = x.x + s4.x;
-  x.y = x.y + s4.y;
-  x.z = x.z + s4.z;
-  x.w = x.w + s4.w;
-  return x;
+  acc.x = acc.x + s4.x;
+  acc.y = acc.y + s4.y;
+  acc.z = acc.z + s4.z;
+  acc.w = acc.w + s4.w;
+  return acc;
 }
 
 template <bool BF16, bool FIRST>
@@ -724,32 +751,43 @@ __global__ __launch_bounds__(kBlock) void fused_acc_mean_kernel(const Segment* _
       }
       if ((any & 15) == 0 && (anys & (BF16 ? 7 : 15)) == 0) {
         const int n4 = len >> 2;
-        for (int i = lane; i < n4; i += 64 * kRtU) {
-          v4f a[kRtU];
-          for (int r0 = 0; r0 < R; r0 += kRtChunk) {
-            v4f x[kRtU][kRtChunk];
+        for (int i = lane; i < n4; i += 64 * kAccMeanU) {
+          v4f a[kAccMeanU];
+          for (int r0 = 0; r0 < R; r0 += kAccMeanChunk) {
+            const float* ap[kAccMeanChunk];
+            const void* sp[kAccMeanChunk];
 #pragma unroll
-            for (int u = 0; u < kRtU; ++u)
+            for (int q = 0; q < kAccMeanChunk; ++q) {
+              const int64_t k = static_cast<int64_t>(r0 + q < R ? r0 + q : 0) * P + g.var;
+              ap[q] = grads[k];
+              sp[q] = steps[k];
+            }
+            v4f x[kAccMeanU][kAccMeanChunk];
+            typename StepRaw<BF16>::T y[kAccMeanU][kAccMeanChunk];
 #pragma unroll
-              for (int q = 0; q < kRtChunk; ++q)
+            for (int u = 0; u < kAccMeanU; ++u)
+#pragma unroll
+              for (int q = 0; q < kAccMeanChunk; ++q)
                 if (r0 + q < R && i + 64 * u < n4) {
-                  const int64_t k = static_cast<int64_t>(r0 + q) * P + g.var;
-                  x[u][q] = acc_step4<BF16, FIRST>(grads[k], steps[k], g.start + 4 * (i + 64 * u));
+                  const int64_t e = g.start + 4 * (i + 64 * u);
+                  x[u][q] = FIRST ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : ld4s(ap[q] + e);
+                  if (sp[q] != nullptr) y[u][q] = step_ld4<BF16>(sp[q], e);
                 }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int u = 0; u < kRtU; ++u) {
+            for (int u = 0; u < kAccMeanU; ++u) {
               if (i + 64 * u < n4) {
 #pragma unroll
-                for (int q = 0; q < kRtChunk; ++q) {
+                for (int q = 0; q < kAccMeanChunk; ++q) {
                   if (r0 + q < R) {
+                    const v4f v = acc_combine4<BF16, FIRST>(x[u][q], y[u][q], sp[q] != nullptr);
                     if (r0 + q == 0) {
-                      a[u] = x[u][q];
+                      a[u] = v;
                     } else {
-                      a[u].x = a[u].x + x[u][q].x;
-                      a[u].y = a[u].y + x[u][q].y;
-                      a[u].z = a[u].z + x[u][q].z;
-                      a[u].w = a[u].w + x[u][q].w;
+                      a[u].x = a[u].x + v.x;
+                      a[u].y = a[u].y + v.y;
+                      a[u].z = a[u].z + v.z;
+                      a[u].w = a[u].w + v.w;
                     }
                   }
                 }
@@ -757,7 +795,7 @@ __global__ __launch_bounds__(kBlock) void fused_acc_mean_kernel(const Segment* _
             }
           }
 #pragma unroll
-          for (int u = 0; u < kRtU; ++u) {
+          for (int u = 0; u < kAccMeanU; ++u) {
             if (i + 64 * u < n4) {
               v4f m;
               m.x = finish_rt(a[u].x, R, scale, pow2 != 0);
@@ -1116,13 +1154,12 @@ class HipLauncher final : public Launcher {
       if ((mode_ == kModeFused || mode_ == kModeBucketView) && !used_active_) {
         const int32_t p2 = pow2_ ? 1 : 0;
         int64_t* st = (flags_ & 1) ? d_stamps_ + static_cast<int64_t>(b) * 4 : nullptr;
-        // No limit on workgroups per CU here: with two streams per replica
-        // (accumulator and step) in chunks of eight replicas, more waves per
-        // CU hide more latency (BERT-base, R = 16: 3.83 ms per synchronising
-        // step against 5.68 at one workgroup per CU).
+        // One workgroup per CU, as for the other streaming kernels (BERT-base,
+        // R = 16, bf16: 3.27-3.29 ms per synchronising step against
+        // 3.33-3.35 with no limit).
 #define DDPB_ACC_MEAN(BF, FI)                                                                                   \
-  hipExtLaunchKernelGGL((fused_acc_mean_kernel<BF, FI>), vgrid, dim3(kBlock), 0, s, t0, t1, 0, d_segs_ + v0, vn, \
-                        d_grads_, steps, P_, R_, scale_, p2, vec_ok_, st)
+  hipExtLaunchKernelGGL((fused_acc_mean_kernel<BF, FI>), vgrid, dim3(kBlock), lds_one_per_cu_, s, t0, t1, 0,    \
+                        d_segs_ + v0, vn, d_grads_, steps, P_, R_, scale_, p2, vec_ok_, st)
         if (sync_step_bf16_) {
           if (sync_step_first_) DDPB_ACC_MEAN(true, true); else DDPB_ACC_MEAN(true, false);
         } else {
