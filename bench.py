@@ -62,6 +62,9 @@ def parse():
     ap.add_argument("--fused-last-step", action="store_true",
                     help="--config 4: the synchronising micro-step is accumulated by the reduction "
                          "itself (ddpb_set_sync_step) instead of a separate accumulation pass")
+    ap.add_argument("--step-lists", action="store_true",
+                    help="--config 4: pass the step tensors as R x P lists on every call instead of "
+                         "step tables checked and marshalled once")
     ap.add_argument("--wg-per-cu", type=int, default=None, choices=[0, 1, 2],
                     help="reduction workgroups per compute unit (0 = no limit); default the "
                          "library's (1), and for --config 5 a sweep of 1 and 0")
@@ -462,25 +465,33 @@ def run_nosync_bench(args, torch, D, WG, WC):
     red.set_workgroups_per_cu(wg_per_cu)
     order = w.ready_order()
     acc_ms = []
+    # The step tensors are the same every optimizer step: check and marshal
+    # their addresses once (about 2 ms of Python per micro-step otherwise,
+    # which makes the loop host-bound); --step-lists passes the lists.
+    step_args = steps if args.step_lists else [red.step_table(steps[t]) for t in range(k)]
+    host_s = []
 
     def one_step(timed):
+        h0 = time.perf_counter()
         for t in range(k):
             if t == k - 1:
                 red.set_sync(True)
                 if args.fused_last_step:       # the sync accumulates this step itself
-                    red.set_sync_step(steps[t], first_step=(t == 0))
+                    red.set_sync_step(step_args[t], first_step=(t == 0))
                     red.sync(order)
                     continue
             e0 = e1 = None
             if timed:
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(compute)
-            red.no_sync_accumulate(steps[t], first_step=(t == 0))
+            red.no_sync_accumulate(step_args[t], first_step=(t == 0))
             if timed:
                 e1.record(compute)
                 acc_ms.append((t, e0, e1))
             red.sync(order)                    # hooks: no-ops until the last micro-step
         red.set_sync(False)
+        if timed:
+            host_s.append(time.perf_counter() - h0)
 
     red.set_sync(False)
     for _ in range(args.warmup):
@@ -511,8 +522,9 @@ def run_nosync_bench(args, torch, D, WG, WC):
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "tensors": P, "params": N, "replicas": R, "micro_steps": k,
                    "step_dtype": "bf16", "buckets": red.num_buckets, "workgroups_per_cu": wg_per_cu,
-                   "fused_last_step": args.fused_last_step,
+                   "fused_last_step": args.fused_last_step, "step_tables": not args.step_lists,
                    "alg_bytes_per_step": alg},
+        "host_ms_per_step": round(1e3 * sum(host_s) / len(host_s), 4),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "accumulate_first_ms": round(sum(acc_first) / len(acc_first), 4),
         "accumulate_ms": round(avg_rest, 4), "sync_busy_ms_last": round(sync_ms, 4),

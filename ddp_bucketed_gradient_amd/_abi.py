@@ -45,6 +45,11 @@ i32, i64, vp = C.c_int32, C.c_int64, C.c_void_p
 P32, P64 = C.POINTER(C.c_int32), C.POINTER(C.c_int64)
 
 
+def ptr_array(ptrs: Sequence[int]):
+    """A void* array of the given addresses (0 = NULL), at least one element long."""
+    return (vp * max(len(ptrs), 1))(*ptrs)
+
+
 def _sig(lib):
     S = {
         "ddpb_reducer_create": [P64, P32, i32, i32, i64, i32, C.POINTER(vp)],
@@ -182,12 +187,14 @@ class Lib:
     def set_sync(self, h, enabled: bool):
         self._check(self.dll.ddpb_set_sync(h, 1 if enabled else 0))
 
-    def no_sync_accumulate(self, h, step_ptrs: Sequence[int], step_dtype: int, first_step: bool):
-        sp = (vp * max(len(step_ptrs), 1))(*[vp(int(p)) if p else vp() for p in step_ptrs])
+    def no_sync_accumulate(self, h, step_ptrs, step_dtype: int, first_step: bool):
+        """step_ptrs: R * P device addresses (0 = no step), or an array made by ptr_array."""
+        sp = step_ptrs if isinstance(step_ptrs, C.Array) else ptr_array(step_ptrs)
         self._check(self.dll.ddpb_no_sync_accumulate(h, sp, step_dtype, 1 if first_step else 0))
 
-    def set_sync_step(self, h, step_ptrs: Sequence[int], step_dtype: int, first_step: bool):
-        sp = (vp * max(len(step_ptrs), 1))(*[vp(int(p)) if p else vp() for p in step_ptrs])
+    def set_sync_step(self, h, step_ptrs, step_dtype: int, first_step: bool):
+        """step_ptrs as for no_sync_accumulate."""
+        sp = step_ptrs if isinstance(step_ptrs, C.Array) else ptr_array(step_ptrs)
         self._check(self.dll.ddpb_set_sync_step(h, sp, step_dtype, 1 if first_step else 0))
 
     def reset(self, h):

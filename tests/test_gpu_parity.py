@@ -566,6 +566,42 @@ def test_config5_overlap_parity(size):
         assert_bits_equal(grads[5][v].cpu().numpy(), want, f"v={v}")
 
 
+def test_step_table_reused_across_micro_steps():
+    """One StepTable (checked and marshalled once) passed to several
+    no_sync_accumulate calls and then as the synchronising step gives the same
+    bits as the oracle fed the same steps each time."""
+    numels = [5000, 3, 8192, 777]
+    R, cap, k = 4, 4 * 6000, 3
+    P = len(numels)
+    say(f"step table reuse R={R} k={k}")
+    red = D.Reducer([(n,) for n in numels], R, cap)
+    grads = alloc_grads(numels, R)
+    red.bind(grads)
+    hs = [[WG.normal(WG.seed_of(13, r, v), n).to(torch.bfloat16) for v, n in enumerate(numels)] for r in range(R)]
+    table = red.step_table([[h.cuda() for h in row] for row in hs])
+    host_steps = [[h.view(torch.int16).numpy().view(np.uint16).copy() for h in row] for row in hs]
+    orc = OR.Reducer(numels, R, cap)
+    og = [[np.zeros(n, np.float32) for n in numels] for _ in range(R)]
+    orc.bind(og)
+    red.set_sync(False)
+    orc.set_sync(False)
+    for t in range(k - 1):
+        red.no_sync_accumulate(table, first_step=(t == 0))
+        orc.no_sync_accumulate(host_steps, first=(t == 0))
+    red.set_sync(True)
+    orc.set_sync(True)
+    red.set_sync_step(table)
+    orc.no_sync_accumulate(host_steps, first=False)
+    order = WG.permutation(14, P)
+    red.sync(order)
+    orc.sync(order)
+    got = snapshot(grads)
+    for v in range(P):
+        for r in range(R):
+            assert_bits_equal(got[v][r], og[r][v], f"step table v={v} r={r}")
+    red.close()
+
+
 def test_wrong_size_step_is_refused_before_any_kernel():
     red = D.Reducer([(4,), (6,)], 2, 0)
     grads = alloc_grads([4, 6], 2)

@@ -351,3 +351,36 @@ def test_missing_library_fails_loudly(tmp_path):
     """No fallback: without the built library the binding raises."""
     with pytest.raises(ImportError, match="no fallback"):
         D.Lib(str(tmp_path / "libddpb.so"))
+
+
+def test_pointer_array_marshalling(host):
+    """The binding's void* arrays: addresses in order, 0 as NULL, never empty;
+    a prebuilt array is accepted wherever a list of addresses is."""
+    from ddp_bucketed_gradient_amd import _abi
+    a = _abi.ptr_array([0x1000, 0, 0x2010])
+    assert len(a) == 3 and [a[0], a[1], a[2]] == [0x1000, None, 0x2010]
+    assert len(_abi.ptr_array([])) == 1
+    red = _reducer(host, [10, 20], 2, 0)
+    _bind_fake(red)
+    fake = [0x2000 + 16 * i for i in range(4)]
+    host.set_sync_step(red.h, _abi.ptr_array(fake), D.BF16, False)
+    red.reset()
+    host.no_sync_accumulate(red.h, _abi.ptr_array(fake), D.F32, True)
+
+
+def test_step_table_checks_before_the_library(host):
+    """Reducer.step_table refuses a wrong R x P layout, a wrong element count,
+    mixed dtypes and host tensors before any address reaches the library."""
+    import torch
+    red = _reducer(host, [4, 6], 2, 0)
+    ok = [[torch.zeros(4), torch.zeros(6)] for _ in range(2)]
+    with pytest.raises(ValueError):
+        red.step_table(ok[:1])                                   # one replica short
+    with pytest.raises(ValueError):
+        red.step_table([[torch.zeros(4)] for _ in range(2)])     # one variable short
+    with pytest.raises(ValueError):
+        red.step_table(ok)                                       # not CUDA tensors
+    with pytest.raises(ValueError):
+        red.step_table([[torch.zeros(4, dtype=torch.float16), None] for _ in range(2)])   # not fp32 / bf16
+    t = red.step_table([[None, None] for _ in range(2)])         # no step anywhere: all NULL
+    assert [t.ptrs[i] for i in range(4)] == [None] * 4 and t.code == D.F32
