@@ -380,7 +380,8 @@ def run_sync_bench(args, torch, D, WG, WC):
         achieved = alg * args.steps / (busy_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                    "traffic": traffic_from_profiles(kernel, w.name),
+                    # stored counters cover every variable used by every replica
+                    "traffic": traffic_from_profiles(kernel, w.name) if used is None else None,
                     "kernel": kernel, "launches": n_launch, "avg_launch_us": round(avg_ms * 1e3, 2),
                     "alg_bytes_per_launch": bytes_per_launch,
                     "busy_us_per_step": round(busy_ms * 1e3 / args.steps, 2),
