@@ -29,6 +29,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -52,6 +53,9 @@ def parse():
     ap.add_argument("--blog-param-mib", type=int, default=4, choices=[1, 4],
                     help="--config 6: the 48 MiB payload as 12 x 4 MiB or 48 x 1 MiB parameters")
     ap.add_argument("--cap-mib", type=float, default=None)
+    ap.add_argument("--replicas", type=int, default=None,
+                    help="--config 2/3/6: replica count instead of the workload's (1..64; above 16 the "
+                         "generic-R kernel runs)")
     ap.add_argument("--mode", choices=["fused", "staged", "view"], default="fused",
                     help="view = gradient_as_bucket_view (gradients live in flat bucket storages)")
     ap.add_argument("--n-side", type=int, default=2,
@@ -233,6 +237,9 @@ def run_sync_bench(args, torch, D, WG, WC):
     if args.cap_mib is not None:
         w = WC.Workload(w.cfg, f"{w.name.split('_cap')[0]}_cap{args.cap_mib:g}", w.params, w.R,
                         cap_bytes=int(args.cap_mib * MiB))
+    if args.replicas is not None:
+        w = WC.Workload(w.cfg, re.sub(r"_r\d+", f"_r{args.replicas}", w.name, count=1), w.params, args.replicas,
+                        cap_bytes=w.cap_bytes)
     params = w.params()
     numels = w.numels()
     P, R = len(numels), w.R
@@ -406,7 +413,7 @@ def run_sync_bench(args, torch, D, WG, WC):
     copy_gbps = hbm_copy_ceiling(torch)
     out = {
         "metric": "grad-sync GB/s and % HBM peak; ms per bucketed sync, BERT-large R=8"
-        if w.cfg == 3 else f"grad-sync GB/s; ms per bucketed sync, {w.name}",
+        if w.cfg == 3 and R == 8 else f"grad-sync GB/s; ms per bucketed sync, {w.name}",
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
