@@ -73,6 +73,8 @@ def parse():
                     help="reduction workgroups per compute unit (0 = no limit); default the "
                          "library's (1), and for --config 5 a sweep of 1 and 0")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--roctx", action="store_true",
+                    help="configs 2/3/6: bind with DDPB_BIND_ROCTX (host-side ranges for rocprofv3 --marker-trace)")
     ap.add_argument("--cpu-sample-gb", type=float, default=24.0,
                     help="cap on the algorithmic bytes (2*R*S) of the oracle's sample")
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0,
@@ -250,6 +252,8 @@ def run_sync_bench(args, torch, D, WG, WC):
     red = D.Reducer([p.shape for p in params], R, w.cap_bytes)
     B = red.num_buckets
     flags = 0 if (args.no_time_launches or args.graph) else D.BIND_TIME_LAUNCHES
+    if args.roctx:
+        flags |= D.BIND_ROCTX
     # The compute stream and the side streams are consecutive streams of
     # torch's pool, so the HIP runtime places them on distinct hardware queues
     # (it hands out its 4 queues round-robin); the legacy null stream stays idle.

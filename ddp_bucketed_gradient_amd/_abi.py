@@ -16,7 +16,7 @@ HOSTONLY_LIB = os.path.join(_HERE, "lib", "libddpb_hostonly.so")
 
 F32, BF16 = 0, 1
 MODE_FUSED, MODE_STAGED = 0, 1
-BIND_DEVICE_TIMESTAMPS, BIND_TIME_LAUNCHES = 1, 2
+BIND_DEVICE_TIMESTAMPS, BIND_TIME_LAUNCHES, BIND_ROCTX = 1, 2, 4
 
 OK, E_ARG, E_INDEX, E_DOUBLE_READY, E_INCOMPLETE, E_STATE, E_HIP, E_NOMEM = 0, -1, -2, -3, -4, -5, -6, -7
 _NAMES = {E_ARG: "E_ARG", E_INDEX: "E_INDEX", E_DOUBLE_READY: "E_DOUBLE_READY",

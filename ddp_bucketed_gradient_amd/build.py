@@ -52,7 +52,7 @@ def build_hip(out: str = HIP_LIB) -> str:
     os.makedirs(os.path.dirname(out), exist_ok=True)
     srcs = [os.path.join(CSRC, s) for s in HOST_SOURCES + ["kernels.hip"]]
     tmp = out + ".tmp"
-    _run([_hipcc()] + HIPCC_FLAGS + srcs + ["-o", tmp])
+    _run([_hipcc()] + HIPCC_FLAGS + srcs + ["-L/opt/rocm/lib", "-lrocprofiler-sdk-roctx", "-o", tmp])
     os.replace(tmp, out)
     return out
 

@@ -41,8 +41,10 @@
 // Short page names are defined in core.hpp.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
+#include <rocprofiler-sdk-roctx/roctx.h>
 
 #include <algorithm>
+#include <cstdio>
 #include <cstring>
 #include <vector>
 
@@ -829,6 +831,23 @@ __global__ __launch_bounds__(kBlock) void fused_acc_mean_kernel(const Segment* _
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// A host-side roctx range over one launcher call (bindings made with
+// DDPB_BIND_ROCTX), so that a marker trace shows when the host issued what.
+class HostRange {
+ public:
+  HostRange(bool on, const char* what) : on_(on) {
+    if (on_) roctxRangePushA(what);
+  }
+  ~HostRange() {
+    if (on_) roctxRangePop();
+  }
+  HostRange(const HostRange&) = delete;
+  HostRange& operator=(const HostRange&) = delete;
+
+ private:
+  bool on_;
+};
+
 // Whether work enqueued on `s` now is being recorded into a graph rather than
 // run. A replayed graph repeats the recorded device work only, so anything
 // that reads host memory at run time (a pinned-staging upload) or whose
@@ -938,6 +957,9 @@ class HipLauncher final : public Launcher {
   }
 
   int launch(int32_t first, int32_t last, int64_t iteration, std::string* err) override {
+    char what[48] = "";
+    if (flags_ & 4) std::snprintf(what, sizeof(what), "ddpb launch %d-%d", first, last);
+    const HostRange range((flags_ & 4) != 0, what);
     const size_t ring = static_cast<size_t>(iteration % kTimeRing) * plan_->B();
     if (flags_ & 2) {
       bool cap = false;
@@ -968,6 +990,7 @@ class HipLauncher final : public Launcher {
   }
 
   int join(std::string* err) override {
+    const HostRange range((flags_ & 4) != 0, "ddpb finalize join");
     for (size_t i = 0; i < side_.size(); ++i) {
       if (!side_used_[i]) continue;
       HIP_OK(hipEventRecord(ev_done_[i], side_[i]), "hipEventRecord(done)");
@@ -978,6 +1001,7 @@ class HipLauncher final : public Launcher {
   }
 
   int accumulate(void* const* step_ptrs, int32_t step_dtype, bool first, std::string* err) override {
+    const HostRange range((flags_ & 4) != 0, "ddpb no_sync_accumulate");
     const size_t nptr = static_cast<size_t>(R_) * P_;
     if (plan_->segs.empty()) return kOk;
     bool cap = false;
@@ -1097,6 +1121,7 @@ class HipLauncher final : public Launcher {
       sync_step_active_ = false;
       return kOk;
     }
+    const HostRange range((flags_ & 4) != 0, "ddpb set_sync_step");
     const size_t n = static_cast<size_t>(R_) * P_;
     bool cap = false;
     if (const int rc = capturing(compute_, &cap, err); rc != kOk) return rc;

@@ -59,8 +59,11 @@ enum {
   DDPB_BIND_DEVICE_TIMESTAMPS = 1, /* kernels stamp start/end device clock into the launch log; a
                                       diagnostic: each workgroup's closing fence and counter update
                                       cost about 10 % of the throughput of a BERT-large sync */
-  DDPB_BIND_TIME_LAUNCHES = 2      /* hipEvents around each bucket's kernels (ddpb_get_launch_times);
+  DDPB_BIND_TIME_LAUNCHES = 2,     /* hipEvents around each bucket's kernels (ddpb_get_launch_times);
                                       about 0.8 % of that throughput */
+  DDPB_BIND_ROCTX = 4              /* host-side roctx ranges around each launch of complete buckets
+                                      ("ddpb launch b0-b1"), the finalize join, no_sync_accumulate and
+                                      set_sync_step, for rocprofv3 --marker-trace; no device work */
 };
 
 /* status codes */

@@ -602,6 +602,43 @@ def test_step_table_reused_across_micro_steps():
     red.close()
 
 
+def test_roctx_ranges_leave_results_unchanged():
+    """A binding with host-side roctx ranges (and launch timing) syncs, accumulates
+    and runs a fused synchronising step with the oracle's bits."""
+    numels = [4097, 10, 100, 8192, 3]
+    R, cap = 4, 4 * 5000
+    P = len(numels)
+    say("roctx ranges")
+    red = D.Reducer([(n,) for n in numels], R, cap)
+    grads = alloc_grads(numels, R)
+    red.bind(grads, flags=D.BIND_ROCTX | D.BIND_TIME_LAUNCHES)
+    host = [[WG.normal(WG.seed_of(17, r, v), n).numpy() for v, n in enumerate(numels)] for r in range(R)]
+    fill_from_host(grads, host)
+    orc = OR.Reducer(numels, R, cap)
+    og = [[h.copy() for h in row] for row in host]
+    orc.bind(og)
+    order = WG.permutation(18, P)
+    red.sync(order)
+    orc.sync(order)
+    hs = [[WG.normal(WG.seed_of(19, r, v), n).numpy() for v, n in enumerate(numels)] for r in range(R)]
+    ds = [[torch.from_numpy(h).cuda() for h in row] for row in hs]
+    red.set_sync(False)
+    orc.set_sync(False)
+    red.no_sync_accumulate(ds, first_step=False)
+    orc.no_sync_accumulate(hs, first=False)
+    red.set_sync(True)
+    orc.set_sync(True)
+    red.set_sync_step(ds)
+    orc.no_sync_accumulate(hs, first=False)
+    red.sync(order)
+    orc.sync(order)
+    got = snapshot(grads)
+    for v in range(P):
+        for r in range(R):
+            assert_bits_equal(got[v][r], og[r][v], f"roctx v={v} r={r}")
+    red.close()
+
+
 def test_wrong_size_step_is_refused_before_any_kernel():
     red = D.Reducer([(4,), (6,)], 2, 0)
     grads = alloc_grads([4, 6], 2)
