@@ -59,7 +59,8 @@ def parse():
     ap.add_argument("--mode", choices=["fused", "staged", "view"], default="fused",
                     help="view = gradient_as_bucket_view (gradients live in flat bucket storages)")
     ap.add_argument("--n-side", type=int, default=2,
-                    help="side streams; buckets go round-robin over them")
+                    help="side streams; buckets go round-robin over them (0: reduce on the compute "
+                         "stream itself, no cross-stream events)")
     ap.add_argument("--launch-blocks", type=int, default=None,
                     help="cap on workgroups per reduction launch (0 = whole GPU); "
                          "default 0, and for --config 5 a sweep")
@@ -258,7 +259,7 @@ def run_sync_bench(args, torch, D, WG, WC):
     # torch's pool, so the HIP runtime places them on distinct hardware queues
     # (it hands out its 4 queues round-robin); the legacy null stream stays idle.
     compute = torch.cuda.Stream()
-    sides = [torch.cuda.Stream() for _ in range(args.n_side)]
+    sides = [torch.cuda.Stream() for _ in range(args.n_side)] if args.n_side > 0 else [compute]
     torch.cuda.set_stream(compute)
     if args.mode == "view":        # gradient_as_bucket_view: gradients are views of flat storages
         views = red.bind_bucket_views(compute_stream=compute, side_streams=sides, flags=flags)
@@ -451,7 +452,7 @@ def run_sync_bench(args, torch, D, WG, WC):
 
 def _pool_streams(torch, n_side):
     compute = torch.cuda.Stream()
-    sides = [torch.cuda.Stream() for _ in range(n_side)]
+    sides = [torch.cuda.Stream() for _ in range(n_side)] if n_side > 0 else [compute]
     torch.cuda.set_stream(compute)
     return compute, sides
 

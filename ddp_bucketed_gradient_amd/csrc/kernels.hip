@@ -969,16 +969,22 @@ class HipLauncher final : public Launcher {
         return kErrState;
       }
     }
-    HIP_OK(hipEventRecord(ev_ready_[first], compute_), "hipEventRecord(ready)");
+    // A bucket whose stream is the compute stream itself is ordered after the
+    // gradients by the stream alone: no ready event, no wait, nothing to join.
+    bool fork = false;
+    for (int32_t b = first; b <= last && !fork; ++b) fork = side_[static_cast<size_t>(b) % side_.size()] != compute_;
+    if (fork) HIP_OK(hipEventRecord(ev_ready_[first], compute_), "hipEventRecord(ready)");
     uint32_t waited = 0;
     for (int32_t b = first; b <= last; ++b) {
       const size_t si = static_cast<size_t>(b) % side_.size();
       hipStream_t s = side_[si];
-      if (!(waited & (1u << si))) {
-        HIP_OK(hipStreamWaitEvent(s, ev_ready_[first], 0), "hipStreamWaitEvent(ready)");
-        waited |= 1u << si;
+      if (s != compute_) {
+        if (!(waited & (1u << si))) {
+          HIP_OK(hipStreamWaitEvent(s, ev_ready_[first], 0), "hipStreamWaitEvent(ready)");
+          waited |= 1u << si;
+        }
+        side_used_[si] = 1;
       }
-      side_used_[si] = 1;
       // Timing events ride on the kernel dispatches themselves (start of the
       // bucket's first kernel, end of its last), not on separate markers.
       hipEvent_t t0 = (flags_ & 2) ? ev_t0_[ring + b] : nullptr;

@@ -139,7 +139,11 @@ int ddpb_workspace_bytes(ddpb_t h, int32_t mode, int64_t* bytes);
  *                  runs on side_streams[b % n_side]. Keep them on hardware
  *                  queues of their own (with 4 queues per process, the
  *                  compute stream and two side streams created one after the
- *                  other are placed apart).
+ *                  other are placed apart). An entry may be the compute stream
+ *                  itself: its buckets then run in order with the compute
+ *                  work, with no cross-stream events (nothing overlaps them;
+ *                  the lowest latency when there is no backward to hide
+ *                  behind).
  *   mode, flags    DDPB_MODE_*, DDPB_BIND_*.
  * Synchronizes the compute stream once to upload the tables. Not allowed
  * while an iteration is in progress. */

@@ -222,6 +222,41 @@ def test_stream_ordering_with_delayed_producer():
             assert_bits_equal(got[v][r], want[r][v], f"v={v} r={r}")
 
 
+@pytest.mark.parametrize("layout", ["compute_only", "compute_and_side"])
+def test_compute_stream_as_side_stream(layout):
+    """Buckets bound to the compute stream itself run without cross-stream
+    events; mixed with a separate side stream, that stream's buckets still wait
+    for a producer delayed on the compute stream, and finalize still joins it."""
+    numels = [4096 * 3 + 5, 999, 50000, 7]
+    R = 4
+    P = len(numels)
+    say(f"compute stream as side stream: {layout}")
+    red = D.Reducer([(n,) for n in numels], R, 0)
+    grads = alloc_grads(numels, R)
+    compute = torch.cuda.current_stream()
+    sides = [compute] if layout == "compute_only" else [compute, torch.cuda.Stream()]
+    red.bind(grads, compute_stream=compute, side_streams=sides, flags=D.BIND_TIME_LAUNCHES)
+    for it in range(2):
+        host = _host_inputs(31 + it, numels, R)
+        staged = [[torch.from_numpy(h).cuda() for h in row] for row in host]
+        torch.cuda.synchronize()
+        a = torch.randn(2048, 2048, device="cuda")
+        for v in range(P - 1, -1, -1):             # reverse index = bucket order
+            for _ in range(30):
+                a = torch.tanh(a @ a * 1e-3)       # delay on the compute stream
+            for r in range(R):
+                grads[r][v].copy_(staged[r][v])
+            red.mark_ready(v)                     # host does not wait
+        red.finalize()
+        got = snapshot(grads)
+        want, _ = _oracle_sync(numels, R, 0, host, list(range(P - 1, -1, -1)))
+        for v in range(P):
+            for r in range(R):
+                assert_bits_equal(got[v][r], want[r][v], f"{layout} it={it} v={v} r={r}")
+        assert len(red.launch_times_ms()) == P
+    red.close()
+
+
 def test_parked_buckets_and_device_stamps():
     numels = [3000] * 12
     R = 2
