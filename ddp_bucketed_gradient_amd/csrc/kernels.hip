@@ -696,9 +696,9 @@ __device__ __forceinline__ typename StepRaw<BF16>::T step_ld4(const void* step, 
 
 // What the accumulation would leave in one replica's gradient: float(step) on
 // a first step, acc + float(step) otherwise; acc where the replica has no step
-// (+0.0 on a first step).
+// (+0.0 on a first step). `raw` is read only when has_step.
 template <bool BF16, bool FIRST>
-__device__ __forceinline__ v4f acc_combine4(v4f acc, typename StepRaw<BF16>::T raw, bool has_step) {
+__device__ __forceinline__ v4f acc_combine4(v4f acc, const typename StepRaw<BF16>::T& raw, bool has_step) {
   if (!has_step) {
     if (FIRST) return v4f{0.0f, 0.0f, 0.0f, 0.0f};
     return acc;
@@ -773,7 +773,7 @@ __global__ __launch_bounds__(kBlock) void fused_acc_mean_kernel(const Segment* _
                 if (r0 + q < R && i + 64 * u < n4) {
                   const int64_t e = g.start + 4 * (i + 64 * u);
                   x[u][q] = FIRST ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : ld4s(ap[q] + e);
-                  if (sp[q] != nullptr) y[u][q] = step_ld4<BF16>(sp[q], e);
+                  if (sp[q] != nullptr) y[u][q] = step_ld4<BF16>(sp[q], e);   // else never read
                 }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
