@@ -230,7 +230,9 @@ def cpu_baseline_threads(w, host_in, nvars_sample, min_seconds, threads):
     return done / dt / 1e9, dt, len(reds), min(reps)
 
 
-def run_sync_bench(args, torch, D, WG, WC):
+def sync_workload(args, WC):
+    """The workload of --config 2, 3 or 6, with --cap-mib and --replicas applied
+    (both also rename it, so stored figures keyed by name do not carry over)."""
     if args.config == 2:
         w = WC.RESNET50
     elif args.config == 6:
@@ -241,8 +243,15 @@ def run_sync_bench(args, torch, D, WG, WC):
         w = WC.Workload(w.cfg, f"{w.name.split('_cap')[0]}_cap{args.cap_mib:g}", w.params, w.R,
                         cap_bytes=int(args.cap_mib * MiB))
     if args.replicas is not None:
+        if not 1 <= args.replicas <= 64:
+            raise SystemExit("bench.py: --replicas must be in 1..64")
         w = WC.Workload(w.cfg, re.sub(r"_r\d+", f"_r{args.replicas}", w.name, count=1), w.params, args.replicas,
                         cap_bytes=w.cap_bytes)
+    return w
+
+
+def run_sync_bench(args, torch, D, WG, WC):
+    w = sync_workload(args, WC)
     params = w.params()
     numels = w.numels()
     P, R = len(numels), w.R

@@ -63,3 +63,38 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "--gpus 1" in r.stderr
     assert r.stdout == ""
+
+
+def _args(argv):
+    old = sys.argv
+    sys.argv = ["bench.py"] + argv
+    try:
+        return bench.parse()
+    finally:
+        sys.argv = old
+
+
+@pytest.mark.parametrize("argv,name,R,cap", [
+    ([], "bert_large_r8_cap25", 8, 25 << 20),
+    (["--config", "2"], "resnet50_r8", 8, 25 << 20),
+    (["--cap-mib", "1"], "bert_large_r8_cap1", 8, 1 << 20),
+    (["--replicas", "32"], "bert_large_r32_cap25", 32, 25 << 20),
+    (["--replicas", "20", "--cap-mib", "0"], "bert_large_r20_cap0", 20, 0),
+    (["--config", "2", "--replicas", "16"], "resnet50_r16", 16, 25 << 20),
+    (["--config", "6", "--blog-param-mib", "1", "--replicas", "8"], "blog48mib_48x1mib_r8", 8, 4 << 20),
+])
+def test_sync_workload_selection(argv, name, R, cap):
+    """--config, --cap-mib and --replicas pick and rename the workload, so a
+    stored traffic figure keyed by name never applies to another setting."""
+    from workloads import configs as WC
+    w = bench.sync_workload(_args(argv), WC)
+    assert (w.name, w.R, w.cap_bytes) == (name, R, cap)
+    assert bench.traffic_from_profiles("fused_mean_kernel", w.name) is None or name in (
+        "bert_large_r8_cap25", "resnet50_r8")
+
+
+def test_replicas_out_of_range_is_refused():
+    from workloads import configs as WC
+    for bad in ("0", "65"):
+        with pytest.raises(SystemExit):
+            bench.sync_workload(_args(["--replicas", bad]), WC)
