@@ -766,15 +766,21 @@ __global__ __launch_bounds__(kBlock) void fused_acc_mean_kernel(const Segment* _
             }
             v4f x[kAccMeanU][kAccMeanChunk];
             typename StepRaw<BF16>::T y[kAccMeanU][kAccMeanChunk];
+            // Every accumulator load of the group first, then every step load:
+            // 7.5 % faster than alternating the two per replica (BERT-base,
+            // R = 16, bf16: 3.01-3.03 against 3.26-3.28 ms).
 #pragma unroll
             for (int u = 0; u < kAccMeanU; ++u)
 #pragma unroll
               for (int q = 0; q < kAccMeanChunk; ++q)
-                if (r0 + q < R && i + 64 * u < n4) {
-                  const int64_t e = g.start + 4 * (i + 64 * u);
-                  x[u][q] = FIRST ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : ld4s(ap[q] + e);
-                  if (sp[q] != nullptr) y[u][q] = step_ld4<BF16>(sp[q], e);   // else never read
-                }
+                if (r0 + q < R && i + 64 * u < n4)
+                  x[u][q] = FIRST ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : ld4s(ap[q] + g.start + 4 * (i + 64 * u));
+#pragma unroll
+            for (int u = 0; u < kAccMeanU; ++u)
+#pragma unroll
+              for (int q = 0; q < kAccMeanChunk; ++q)
+                if (r0 + q < R && i + 64 * u < n4 && sp[q] != nullptr)   // else never read
+                  y[u][q] = step_ld4<BF16>(sp[q], g.start + 4 * (i + 64 * u));
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int u = 0; u < kAccMeanU; ++u) {
