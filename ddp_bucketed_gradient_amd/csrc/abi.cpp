@@ -252,7 +252,8 @@ int ddpb_no_sync_accumulate(ddpb_t h, void* const* step_ptrs, int32_t step_dtype
 
 int ddpb_reset(ddpb_t h) {
   if (!h) return fail(DDPB_E_ARG, "NULL handle");
-  return h->red.reset();
+  std::string err;
+  return pass(h->red.reset(&err), err);
 }
 
 int ddpb_get_launch_log(ddpb_t h, int32_t* buckets, int32_t* trigger_call, int64_t* dev_t0,

@@ -157,6 +157,10 @@ int Reducer::set_sync_step(void* const* step_ptrs, int32_t step_dtype, bool firs
     *err = "set_sync_step: bad step pointers or dtype";
     return kErrArg;
   }
+  if (failed_) {
+    *err = "the previous iteration left buckets unreduced; a new iteration cannot start before ddpb_reset";
+    return kErrIncomplete;
+  }
   if (iteration_open()) {
     *err = "set_sync_step: must come before the iteration's hooks";
     return kErrState;
@@ -194,6 +198,11 @@ int Reducer::finalize(std::string* err) {
   }
   if (failed_ || next_bucket_ != plan_.B()) {
     failed_ = true;
+    // The buckets already launched keep running on the side streams: order
+    // later compute-stream work (the caller's recovery, the next backward's
+    // gradient writes) after them, so nothing races with their copy-back.
+    std::string e2;
+    launcher_->join(&e2);
     *err = "finalize: not every bucket was reduced in this iteration (" +
            std::to_string(next_bucket_) + " of " + std::to_string(plan_.B()) + " launched)";
     return kErrIncomplete;
@@ -239,6 +248,16 @@ int Reducer::accumulate(void* const* step_ptrs, int32_t step_dtype, bool first, 
     *err = "no_sync_accumulate: bad step pointers or dtype";
     return kErrArg;
   }
+  if (failed_) {
+    *err = "the previous iteration left buckets unreduced; a new iteration cannot start before ddpb_reset";
+    return kErrIncomplete;
+  }
+  if (iteration_open()) {
+    // Buckets of the open iteration may still be reducing on the side streams;
+    // an accumulation on the compute stream would race with their copy-back.
+    *err = "no_sync_accumulate: an iteration is in progress (finalize it first)";
+    return kErrState;
+  }
   return launcher_->accumulate(step_ptrs, step_dtype, first, err);
 }
 
@@ -264,11 +283,25 @@ int Reducer::rebuild_buckets(int64_t cap_bytes, std::string* err) {
   return kOk;
 }
 
-int Reducer::reset() {
+// Recovery after a failed or abandoned iteration. Buckets already launched keep
+// running; the compute stream is made to wait for them, so that work the
+// caller enqueues next cannot race with their copy-back. Everything the failed
+// synchronisation held is dropped with it: its used flags (which serve one
+// synchronising iteration, [Li] "Gradient Accumulation (no_sync)") and its
+// synchronising step.
+int Reducer::reset(std::string* err) {
   failed_ = false;
   drop_sync_step();
+  int rc = kOk;
+  if (bound_) rc = launcher_->join(err);
+  if (used_set_) {
+    std::string e2;
+    launcher_->set_used(nullptr, nullptr, &e2);
+  }
+  used_set_ = false;
+  used_acc_.clear();
   begin_iteration();
-  return kOk;
+  return rc;
 }
 
 }  // namespace ddpb

@@ -157,7 +157,7 @@ class Reducer {
   int finalize(std::string* err);
   int set_sync(bool enabled, std::string* err);
   int accumulate(void* const* step_ptrs, int32_t step_dtype, bool first, std::string* err);
-  int reset();
+  int reset(std::string* err);
   // [C30] "第一次迭代为何不同": re-plan from the hook order of the last finished
   // iteration (same cap rule); the handle must be bound again afterwards.
   int rebuild_buckets(int64_t cap_bytes, std::string* err);

@@ -241,7 +241,8 @@ int ddpb_mark_ready(ddpb_t h, int32_t v);
 int ddpb_mark_ready_many(ddpb_t h, const int32_t* vs, int32_t n);
 
 /* End of backward: every bucket must have been launched (else
- * DDPB_E_INCOMPLETE, latched). Records a completion event on every side
+ * DDPB_E_INCOMPLETE, latched; the compute stream is then still made to wait
+ * for the buckets that did launch). Records a completion event on every side
  * stream and makes the compute stream wait for them, so later work on the
  * compute stream sees the averaged gradients without a host synchronization;
  * then resets the per-iteration state. A no-op while sync is disabled and no
@@ -272,7 +273,10 @@ int ddpb_set_sync(ddpb_t h, int32_t enabled);
  *   step_ptrs   R*P device pointers (replica-major), numel[v] elements each;
  *               NULL = that replica produced no gradient for the variable in
  *               this backward (zeros on the first step, unchanged otherwise)
- *   step_dtype  DDPB_F32 or DDPB_BF16 (widened exactly to fp32) */
+ *   step_dtype  DDPB_F32 or DDPB_BF16 (widened exactly to fp32)
+ * Belongs between iterations: DDPB_E_STATE while an iteration is in progress
+ * (its buckets may still be reducing on the side streams), DDPB_E_INCOMPLETE
+ * while a failed iteration is latched. */
 int ddpb_no_sync_accumulate(ddpb_t h, void* const* step_ptrs, int32_t step_dtype,
                             int32_t first_step);
 
@@ -289,7 +293,7 @@ int ddpb_no_sync_accumulate(ddpb_t h, void* const* step_ptrs, int32_t step_dtype
  * stay valid until ddpb_finalize.
  *   step_ptrs, step_dtype, first_step   as for ddpb_no_sync_accumulate
  * Must come before the iteration's first ddpb_mark_ready, with sync enabled
- * (else DDPB_E_STATE); consumed by that iteration's ddpb_finalize, dropped by
+ * (else DDPB_E_STATE; DDPB_E_INCOMPLETE while a failed iteration is latched); consumed by that iteration's ddpb_finalize, dropped by
  * ddpb_reset, a rebind or a rebuild. While it is set, ddpb_set_sync(h, 0) is
  * refused. Fused and bucket-view modes reduce each bucket in one kernel; in
  * staged mode, or with used flags, each bucket's variables are accumulated
@@ -320,8 +324,14 @@ int ddpb_set_sync_step(ddpb_t h, void* const* step_ptrs, int32_t step_dtype,
  * iteration is in progress. */
 int ddpb_set_local_used(ddpb_t h, const uint8_t* used);
 
-/* Clears a latched DDPB_E_INCOMPLETE and the per-iteration state. Buckets
- * already enqueued keep running. */
+/* Recovery after a failed or abandoned iteration ([TP] "When a parameter never
+ * receives a gradient": the failure surfaces at the next forward; clearing it
+ * is this library's call). Clears a latched DDPB_E_INCOMPLETE, the
+ * per-iteration state, the used flags set for the failed synchronisation
+ * (ddpb_set_local_used) and a pending ddpb_set_sync_step. Buckets already
+ * enqueued keep running; the compute stream is made to wait for every side
+ * stream that ran one, so work enqueued on it afterwards cannot race with
+ * their copy-back. Errors: DDPB_E_HIP. */
 int ddpb_reset(ddpb_t h);
 
 /* ---------------------------------------------------------------------------

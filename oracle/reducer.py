@@ -283,7 +283,13 @@ class Reducer:
         self._reset_iteration()
 
     def reset(self):
+        """Recovery after a failed iteration (the failure itself surfaces at
+        the next forward, [TP] "When a parameter never receives a gradient").
+        The used flags served the synchronisation that failed and are dropped
+        with it: they serve one synchronising iteration ([Li] "Gradient
+        Accumulation (no_sync)")."""
         self.failed = False
+        self.used_acc = None
         self._reset_iteration()
 
     # -- no_sync -------------------------------------------------------------
@@ -292,7 +298,16 @@ class Reducer:
         micro-step, ``grad += step`` afterwards (float32). ``step`` holds
         float32 arrays, or uint16 arrays of bf16 bit patterns; ``None`` means
         that replica produced no gradient for that variable (it contributes
-        zeros)."""
+        zeros).
+
+        A local backward belongs between iterations: inside an open iteration
+        (its first hook ran, finalize did not) it is refused, and so it is
+        while a failed iteration is latched ([TP] "When a parameter never
+        receives a gradient": the next iteration cannot start)."""
+        if self.failed:
+            raise ReductionIncomplete("prior iteration did not finish reducing every bucket")
+        if self.started:
+            raise RuntimeError("no_sync_accumulate: an iteration is in progress")
         for r in range(self.R):
             for v in range(self.P):
                 s = step[r][v]

@@ -217,3 +217,60 @@ def test_unused_bert_large_sampled():
         for r in (0, R - 1):
             assert_bits_equal(grads[r][v].cpu().numpy(), og[r][0], f"v={v} r={r}")
     assert [b for b, _ in red.launch_log()] == list(range(red.num_buckets))
+
+
+@pytest.mark.parametrize("mode", [D.MODE_FUSED, D.MODE_STAGED])
+def test_reset_after_failed_iteration_drops_flags(mode):
+    """An iteration with used flags fails (half of its hooks fire, finalize
+    refuses), the reducer is reset, and the next synchronisation runs with
+    other flags: its result is the oracle's under the new flags alone (the
+    failed iteration's flags are not OR-ed in), bit for bit."""
+    R, P, cap = 4, len(NUMELS), 4 * 15000
+    say(f"reset after a failed iteration with flags, mode={mode}")
+    red = D.Reducer([(n,) for n in NUMELS], R, cap)
+    grads = alloc_grads(NUMELS, R)
+    red.bind(grads, mode=mode)
+    orc = OR.Reducer(NUMELS, R, cap)
+    og = [[np.zeros(n, np.float32) for n in NUMELS] for _ in range(R)]
+    orc.bind(og)
+    host = _host(31, R)
+    fill_from_host(grads, host)
+    for r in range(R):
+        for v in range(P):
+            og[r][v][...] = host[r][v]
+    used_a = _flags(301 + mode, R, P)
+    red.set_local_used(used_a)
+    orc.set_local_used(used_a)
+    first = [v for v in WG.permutation(32, P) if used_a.any(axis=0)[v]]
+    first = first[:len(first) // 2]
+    for v in first:
+        red.mark_ready(v)
+        orc.mark_ready(v)
+    with pytest.raises(D.DdpbError) as e:
+        red.finalize()
+    assert e.value.code == D.E_INCOMPLETE
+    with pytest.raises(OR.ReductionIncomplete):
+        orc.finalize()
+    red.reset()
+    orc.reset()
+    torch.cuda.synchronize()
+    host = _host(33, R)
+    fill_from_host(grads, host)
+    for r in range(R):
+        for v in range(P):
+            og[r][v][...] = host[r][v]
+    used_b = _flags(302 + mode, R, P)
+    used_b[:, 0] = True                   # used by every replica now (unused by all before)
+    G = used_b.any(axis=0)
+    order = [v for v in WG.permutation(34, P) if G[v]]
+    red.set_local_used(used_b)
+    orc.set_local_used(used_b)
+    orc.launch_log.clear()
+    red.sync(order)
+    orc.sync(order)
+    got = snapshot(grads)
+    assert red.launch_log() == orc.launch_log
+    for v in range(P):
+        for r in range(R):
+            assert_bits_equal(got[v][r], og[r][v], f"after reset v={v} r={r}")
+    red.close()

@@ -399,3 +399,86 @@ def test_bind_flags(host):
         with pytest.raises(D.DdpbError) as e:
             red.bind_ptrs(ptrs, side_streams=[0], flags=bad)
         assert e.value.code == D.E_ARG
+
+
+def _joins(host):
+    f = host.dll.ddpb_hostonly_join_count
+    f.restype = __import__("ctypes").c_longlong
+    return f()
+
+
+def test_accumulate_refused_inside_an_open_or_failed_iteration(host):
+    """A local backward's accumulation runs on the compute stream; inside an
+    open iteration (buckets may still be reducing on the side streams) it is
+    refused, and while a failed iteration is latched it fails like the hooks.
+    The oracle refuses the same way."""
+    from oracle import reducer as OR
+    numels = [4, 4, 4]
+    red = _reducer(host, numels, 2, 16)
+    _bind_fake(red)
+    orc = OR.Reducer(numels, 2, 16)
+    orc.bind([[np.zeros(n, np.float32) for n in numels] for _ in range(2)])
+    steps = [[np.zeros(n, np.float32) for n in numels] for _ in range(2)]
+    fake = _abi.ptr_array([0x3000 + 64 * i for i in range(2 * len(numels))])
+    red.mark_ready(2)
+    orc.mark_ready(2)
+    with pytest.raises(D.DdpbError) as e:
+        host.no_sync_accumulate(red.h, fake, D.F32, False)
+    assert e.value.code == _abi.E_STATE
+    with pytest.raises(RuntimeError):
+        orc.no_sync_accumulate(steps, first=False)
+    for side in (red.finalize, orc.finalize):
+        with pytest.raises((D.DdpbError, OR.ReductionIncomplete)):
+            side()
+    with pytest.raises(D.DdpbError) as e:
+        host.no_sync_accumulate(red.h, fake, D.F32, False)
+    assert e.value.code == _abi.E_INCOMPLETE
+    with pytest.raises(OR.ReductionIncomplete):
+        orc.no_sync_accumulate(steps, first=False)
+    with pytest.raises(D.DdpbError) as e:
+        host.set_sync_step(red.h, fake, D.F32, False)
+    assert e.value.code == _abi.E_INCOMPLETE
+    red.reset()
+    orc.reset()
+    host.no_sync_accumulate(red.h, fake, D.F32, False)
+    orc.no_sync_accumulate(steps, first=False)
+
+
+def test_reset_and_failed_finalize_join_the_side_streams(host):
+    """Buckets launched before a failure keep running; a failed finalize and a
+    reset make the compute stream wait for the side streams so that later work
+    cannot race with their copy-back."""
+    red = _reducer(host, [4, 4, 4], 2, 16)
+    _bind_fake(red)
+    red.mark_ready(2)                            # bucket 0 launches
+    j0 = _joins(host)
+    with pytest.raises(D.DdpbError):
+        red.finalize()
+    assert _joins(host) == j0 + 1
+    red.reset()
+    assert _joins(host) == j0 + 2
+    red.sync()
+    assert _joins(host) == j0 + 3
+
+
+def test_reset_drops_used_flags(host):
+    """Used flags belong to the synchronisation they were set for; after a
+    failed iteration and a reset, the next iteration expects every variable
+    again (stale flags would mark variable 1 ready by themselves and refuse its
+    hook as a double ready). The oracle agrees."""
+    from oracle import reducer as OR
+    numels = [4, 4]
+    red = _reducer(host, numels, 2, 0)
+    _bind_fake(red)
+    orc = OR.Reducer(numels, 2, 0)
+    orc.bind([[np.zeros(n, np.float32) for n in numels] for _ in range(2)])
+    used = [[True, False], [True, False]]
+    red.set_local_used(used)
+    orc.set_local_used(used)
+    red.mark_ready(0)
+    orc.mark_ready(0)
+    red.reset()                                   # abandon it: the flags go with it
+    orc.reset()
+    red.sync([1, 0])
+    orc.sync([1, 0])
+    assert red.launch_log() == orc.launch_log[-2:] == [(0, 0), (1, 1)]

@@ -1,7 +1,7 @@
 """Differential fuzz of the native readiness state machine (host-only build)
 against the oracle: random sequences of hooks (repeated and out-of-range ones
-included), finalize, no_sync toggles, used flags, ready-order rebuilds, resets
-and next-forward checks. After every operation both sides must have succeeded
+included), finalize, no_sync toggles, local accumulations, used flags,
+ready-order rebuilds, resets and next-forward checks. After every operation both sides must have succeeded
 or failed with the same kind of error, and every finished iteration must have
 launched the same buckets at the same hook calls."""
 import os
@@ -72,7 +72,7 @@ def _run(host, seed):
     trace = []
     for step in range(60):
         op = rng.choice(["hook", "hook", "hook", "hook", "finalize", "used", "sync", "rebuild", "reset",
-                         "forward"], p=[.15, .15, .15, .15, .12, .08, .06, .05, .04, .05])
+                         "forward", "accumulate"], p=[.14, .14, .14, .14, .12, .08, .06, .05, .04, .05, .04])
         if op == "hook":
             v = int(rng.integers(-1, P + 1))
             kn, ko, _, _ = _both(lambda: red.mark_ready(v), lambda: orc.mark_ready(v))
@@ -105,6 +105,12 @@ def _run(host, seed):
                 assert red.buckets() == orc.buckets, (seed, step)
                 bind()
                 log_start = len(orc.launch_log)
+        elif op == "accumulate":
+            first = bool(rng.integers(0, 2))
+            fake = _abi.ptr_array([0x9000 + 64 * i for i in range(R * P)])
+            steps = [[np.zeros(n, np.float32) for n in numels] for _ in range(R)]
+            kn, ko, _, _ = _both(lambda: host.no_sync_accumulate(red.h, fake, D.F32, first),
+                                 lambda: orc.no_sync_accumulate(steps, first))
         elif op == "reset":
             kn, ko, _, _ = _both(red.reset, orc.reset)
             log_start = len(orc.launch_log)
