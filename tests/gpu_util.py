@@ -53,3 +53,41 @@ def assert_bits_equal(got, want, what=""):
         raise AssertionError(f"bit mismatch {what}: {int(diff.sum())} of {g.size} elements, first at {i}: "
                              f"got {got.reshape(-1)[i]!r} ({g.reshape(-1)[i]:#010x}) "
                              f"want {want.reshape(-1)[i]!r} ({w.reshape(-1)[i]:#010x})")
+
+
+def host_workers():
+    """Threads for the oracle's host work (NumPy releases the GIL in its array
+    operations): the process's cores, at most 16."""
+    import os
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def closed_form_launch_log(buckets, order):
+    """The launch log the in-order rule implies for a hook order: bucket b
+    completes at the call c_b that marks its last member, and launches at call
+    max(c_0 .. c_b) (pinned against brute force in the oracle tests)."""
+    pos = {v: i for i, v in enumerate(order)}
+    log, trig = [], -1
+    for b, members in enumerate(buckets):
+        trig = max(trig, max(pos[v] for v in members))
+        log.append((b, trig))
+    return log
+
+
+def to_device_f32(want_host, device="cuda"):
+    """Upload the oracle's expected values (host float32) once, for several
+    assert_device_bits_equal calls."""
+    return torch.from_numpy(np.ascontiguousarray(want_host, dtype=np.float32).reshape(-1)).to(device)
+
+
+def assert_device_bits_equal(got_dev, want, what=""):
+    """Bit patterns of a device tensor against the oracle's expected values
+    (a host float32 array, or its upload by to_device_f32), element by element:
+    compared as int32 on the device; on a mismatch the tensor is copied back and
+    the first difference reported. (No NaN occurs in the full-size inputs.)"""
+    want_dev = want if isinstance(want, torch.Tensor) else to_device_f32(want, got_dev.device)
+    g = got_dev.reshape(-1)
+    if g.numel() == want_dev.numel() and torch.equal(g.view(torch.int32), want_dev.view(torch.int32)):
+        return
+    assert_bits_equal(g.cpu().numpy(), want_dev.cpu().numpy(), what)
+    raise AssertionError(f"device comparison failed but host comparison passed {what}")

@@ -77,25 +77,3 @@ def test_bucket_view_no_sync_with_unaligned_views():
     for r in range(R):
         for v in range(len(numels)):
             assert_bits_equal(views[r][v].cpu().numpy(), orc.views()[r][v], f"r={r} v={v}")
-
-
-def test_bucket_view_bert_large_sampled():
-    w = WC.BERT_LARGE
-    numels = w.numels()
-    R = w.R
-    say(f"bucket view {w.name}")
-    red = D.Reducer([p.shape for p in w.params()], R, w.cap_bytes)
-    views = red.bind_bucket_views()
-    for r in range(R):
-        for v, n in enumerate(numels):
-            WG.normal(WG.seed_of(3, r, v), n, "cuda", out=views[r][v].view(-1))
-    torch.cuda.synchronize()
-    sample = [0, 1, 2, 3, 4, 100, 200, 388, 389, 390]
-    before = {v: [views[r][v].cpu().numpy().reshape(-1) for r in range(R)] for v in sample}
-    red.sync(w.ready_order())
-    torch.cuda.synchronize()
-    for v in range(len(numels)):
-        for r in range(1, R):
-            assert torch.equal(views[r][v], views[0][v]), (v, r)
-    for v in sample:
-        assert_bits_equal(views[2][v].cpu().numpy().reshape(-1), OR.fixed_order_mean(before[v]), f"v={v}")

@@ -2,9 +2,9 @@
 bit for bit (0 ULP) on the same seeded inputs.
 
 Small cases span several segments and ragged tails and run the whole oracle;
-the full-size workloads compare every element where the oracle can afford it
-(ResNet-50 shapes) or sampled tensors plus replica-equality over everything
-(BERT-large, BERT-base no_sync) in the launch configuration the bench times.
+ResNet-50 shapes run at full size here, every element. The other full-size
+workloads (BERT-large with the cap sweep, bucket views and used flags, BERT-base
+no_sync, the overlapped MLP backward) are in test_gpu_fullsize.py.
 """
 import numpy as np
 import pytest
@@ -380,61 +380,6 @@ def test_config2_resnet50_full():
             assert_bits_equal(got[v][r], want[r][v], f"v={v} r={r}")
 
 
-BERT_SAMPLE = [0, 1, 2, 3, 4, 5, 12, 13, 16, 17, 100, 200, 385, 386, 388, 389, 390]
-
-
-@pytest.mark.parametrize("cap_mib", [25, 0, 1, 5, 10, 50, 100, 200])
-def test_config3_bert_large_sampled(cap_mib):
-    w = WC.bert_large_cap(cap_mib)
-    numels = w.numels()
-    say(f"{w.name}: P={len(numels)} R={w.R}")
-    red = D.Reducer([p.shape for p in w.params()], w.R, w.cap_bytes)
-    grads = alloc_grads(numels, w.R)
-    red.bind(grads)
-    _device_inputs(w.cfg, grads)
-    before = snapshot(grads, BERT_SAMPLE)
-    red.sync(w.ready_order())
-    torch.cuda.synchronize()
-    for v in range(len(numels)):            # every replica identical everywhere
-        for r in range(1, w.R):
-            assert torch.equal(grads[r][v], grads[0][v]), (v, r)
-    for v in BERT_SAMPLE:
-        want = OR.fixed_order_mean(before[v])
-        assert_bits_equal(grads[3][v].cpu().numpy(), want, f"v={v}")
-    assert [b for b, _ in red.launch_log()] == list(range(red.num_buckets))
-
-
-def test_config4_bert_base_nosync_sampled():
-    w = WC.BERT_BASE_NOSYNC
-    numels = w.numels()
-    R, k = w.R, w.micro_steps
-    say(f"{w.name}: P={len(numels)} R={R} k={k}")
-    red = D.Reducer([p.shape for p in w.params()], R, w.cap_bytes)
-    assert red.num_buckets == 13
-    grads = alloc_grads(numels, R)
-    red.bind(grads)
-    sample = [0, 1, 5, 6, 100, 197, 198]
-    hs = {v: [] for v in sample}
-    red.set_sync(False)
-    for t in range(k):
-        steps = [[WG.normal(WG.seed_of(4, r, v, t), n, "cuda").to(torch.bfloat16) for v, n in enumerate(numels)]
-                 for r in range(R)]
-        for v in sample:
-            hs[v].append([steps[r][v].view(torch.int16).cpu().numpy().view(np.uint16) for r in range(R)])
-        if t == k - 1:
-            red.set_sync(True)
-        red.no_sync_accumulate(steps, first_step=(t == 0))
-        red.sync(w.ready_order())
-        del steps
-    torch.cuda.synchronize()
-    for v in range(len(numels)):
-        for r in range(1, R):
-            assert torch.equal(grads[r][v], grads[0][v]), (v, r)
-    for v in sample:
-        want = _oracle_nosync_one(hs[v], R, k)
-        assert_bits_equal(grads[R - 1][v].cpu().numpy(), want[0], f"v={v}")
-
-
 @pytest.mark.parametrize("mode", [D.MODE_FUSED, D.MODE_STAGED])
 @pytest.mark.parametrize("blocks", [1, 3])
 def test_capped_grid_parity(mode, blocks):
@@ -529,76 +474,6 @@ def test_two_handles_interleaved_on_shared_streams():
                 assert_bits_equal(got[v][r], wants[k][r][v], f"handle {k} v={v} r={r}")
     for red in reds:
         red.close()
-
-
-def _mlp_backward(params, g0, X, H, W1, W2, dY0, hook):
-    """Backward of [Linear(d, f), Linear(f, d)] blocks in bf16, last layer
-    first; fp32 gradients of replica 0 are written in place."""
-    L = len(X)
-    dY = dY0
-    for l in range(L - 1, -1, -1):
-        vW1, vb1, vW2, vb2 = 4 * l, 4 * l + 1, 4 * l + 2, 4 * l + 3
-        torch.sum(dY, dim=0, dtype=torch.float32, out=g0[vb2])
-        hook(vb2)
-        torch.mm(dY.t(), H[l], torch.float32, out=g0[vW2])
-        hook(vW2)
-        dH = torch.mm(dY, W2[l])
-        torch.sum(dH, dim=0, dtype=torch.float32, out=g0[vb1])
-        hook(vb1)
-        torch.mm(dH.t(), X[l], torch.float32, out=g0[vW1])
-        hook(vW1)
-        dY = torch.mm(dH, W1[l])
-
-
-@pytest.mark.parametrize("size", ["small", "full"])
-def test_config5_overlap_parity(size):
-    """Replica 0's gradients come from a bf16 backward on the compute stream,
-    layer by layer, each hook right after its gradient is written; buckets are
-    reduced on two side streams meanwhile."""
-    if size == "small":
-        L, d, f, T, cap = 3, 256, 1024, 512, 4 * 300000
-        sample = None
-    else:
-        L, d, f, T, cap = 24, 2048, 8192, 8192, WC.MLP_OVERLAP.cap_bytes
-        sample = {95, 94, 93, 92, 1, 0}
-    params = WS.mlp(L, d, f)
-    numels = WS.numels(params)
-    P, R = len(numels), 8
-    say(f"config5 {size}: L={L} d={d} f={f} T={T} P={P}")
-    comp = torch.cuda.Stream()
-    sides = [torch.cuda.Stream(), torch.cuda.Stream()]
-    with torch.cuda.stream(comp):
-        grads = alloc_grads(numels, R)
-        for r in range(1, R):
-            for v, n in enumerate(numels):
-                WG.normal(WG.seed_of(5, r, v), n, "cuda", out=grads[r][v])
-        g = torch.Generator(device="cuda").manual_seed(5)
-        bf = torch.bfloat16
-        X = [torch.randn(T, d, device="cuda", dtype=bf, generator=g) for _ in range(L)]
-        H = [torch.randn(T, f, device="cuda", dtype=bf, generator=g) for _ in range(L)]
-        W1 = [torch.randn(f, d, device="cuda", dtype=bf, generator=g) * 0.02 for _ in range(L)]
-        W2 = [torch.randn(d, f, device="cuda", dtype=bf, generator=g) * 0.02 for _ in range(L)]
-        dY0 = torch.randn(T, d, device="cuda", dtype=bf, generator=g)
-        red = D.Reducer([p.shape for p in params], R, cap)
-        red.bind(grads, compute_stream=comp, side_streams=sides)
-        g0 = [grads[0][v].view(params[v].shape) for v in range(P)]
-        pre = {}
-
-        def hook(v):
-            if sample is None or v in sample:
-                pre[v] = [grads[r][v].cpu().numpy() for r in range(R)]   # before its bucket can launch
-            red.mark_ready(v)
-
-        _mlp_backward(params, g0, X, H, W1, W2, dY0, hook)
-        red.finalize()
-        torch.cuda.synchronize()
-    assert [b for b, _ in red.launch_log()] == list(range(red.num_buckets))
-    for v in range(P):
-        for r in range(1, R):
-            assert torch.equal(grads[r][v], grads[0][v]), (v, r)
-    for v, bufs in pre.items():
-        want = OR.fixed_order_mean(bufs)
-        assert_bits_equal(grads[5][v].cpu().numpy(), want, f"v={v}")
 
 
 def test_step_table_reused_across_micro_steps():

@@ -168,57 +168,6 @@ def test_every_variable_unused(mode):
             assert_bits_equal(got[v][r], host[r][v], f"v={v} r={r}")   # untouched
 
 
-def test_unused_bert_large_sampled():
-    """BERT-large shapes, R = 8, cap 25 MiB, in the bench's launch setup, with
-    some variables unused by single replicas and some by all of them. Sampled
-    variables are checked against the oracle (elementwise, so a one-variable
-    oracle reducer with the same flags gives the same bits); every globally
-    used variable must end equal on all replicas and every globally unused one
-    untouched."""
-    from workloads import configs as WC
-    w = WC.BERT_LARGE
-    numels = w.numels()
-    P, R = len(numels), w.R
-    say(f"{w.name} unused: P={P} R={R}")
-    used = np.ones((R, P), bool)
-    for v in range(P):
-        if v % 7 == 3:
-            used[v % R, v] = False               # one replica skips it
-        if v % 11 == 5:
-            used[(v + 1) % R, v] = False
-    for v in (5, 100, 389):
-        used[:, v] = False                      # no replica uses it
-    G = used.any(axis=0)
-    sample = sorted(set([0, 1, 2, 3, 5, 10, 16, 17, 24, 100, 200, 385, 386, 388, 389, 390]))
-    red = D.Reducer([p.shape for p in w.params()], R, w.cap_bytes)
-    grads = alloc_grads(numels, R)
-    red.bind(grads)
-    for r, row in enumerate(grads):
-        for v, g in enumerate(row):
-            WG.normal(WG.seed_of(w.cfg, r, v), g.numel(), "cuda", out=g)
-    unused_vs = [v for v in range(P) if not G[v]]
-    before = snapshot(grads, sorted(set(sample) | set(unused_vs)))
-    red.set_local_used(used)
-    red.sync([v for v in w.ready_order() if G[v]])
-    torch.cuda.synchronize()
-    for v in range(P):
-        if G[v]:
-            for r in range(1, R):
-                assert torch.equal(grads[r][v], grads[0][v]), (v, r)
-    for v in unused_vs:
-        for r in range(R):
-            assert_bits_equal(grads[r][v].cpu().numpy(), before[v][r], f"unused v={v} r={r}")
-    for v in sample:
-        orc = OR.Reducer([numels[v]], R, 0)
-        og = [[before[v][r].copy()] for r in range(R)]
-        orc.bind(og)
-        orc.set_local_used(used[:, v:v + 1])
-        orc.sync([0] if G[v] else [])
-        for r in (0, R - 1):
-            assert_bits_equal(grads[r][v].cpu().numpy(), og[r][0], f"v={v} r={r}")
-    assert [b for b, _ in red.launch_log()] == list(range(red.num_buckets))
-
-
 @pytest.mark.parametrize("mode", [D.MODE_FUSED, D.MODE_STAGED])
 def test_reset_after_failed_iteration_drops_flags(mode):
     """An iteration with used flags fails (half of its hooks fire, finalize

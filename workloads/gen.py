@@ -5,7 +5,9 @@ Nothing here computes any step of the bucketing method: it only draws numbers.
 Every tensor (replica r, micro-step t, variable v) has its own seed, so any one
 of them can be regenerated on its own.
 
-Seed recipe: ``seed = cfg * 10**9 + t * 10**7 + r * 10**4 + v``.
+Seed recipe: ``seed = cfg * 10**9 + t * 10**7 + r * 10**4 + v``. A whole
+replica's set of step gradients drawn as one flat buffer (``flat_step``) takes
+the variable slot ``FLAT_V`` = 9999, which no model here reaches.
 Values: N(0, sigma) with sigma = 1e-3 (the standard deviation), drawn in fp32
 with ``torch.randn`` from ``torch.Generator(device).manual_seed(seed)`` and
 scaled by sigma. The CPU and the GPU generators produce different streams for
@@ -48,6 +50,27 @@ def normal(seed: int, numel: int, device="cpu", sigma: float = SIGMA,
         raise ValueError("out must be fp32 with numel elements")
     torch.randn(numel, generator=g, device=out.device, dtype=torch.float32, out=flat)
     return flat.mul_(sigma)
+
+
+FLAT_V = 9999
+
+
+def flat_step(cfg: int, r: int, t: int, numel: int, device="cpu", dtype=torch.bfloat16) -> torch.Tensor:
+    """Every variable's step gradient of replica r at micro-step t as one flat
+    N(0, sigma) draw of ``numel`` (the model's total) elements, rounded to
+    ``dtype``; variable v is the slice at the prefix sum of the numels before
+    it. Three device dispatches per (r, t) instead of three per tensor."""
+    x = normal(seed_of(cfg, r, FLAT_V, t), numel, device)
+    return x if dtype == torch.float32 else x.to(dtype)
+
+
+def flat_views(flat: torch.Tensor, numels: Sequence[int]) -> List[torch.Tensor]:
+    """Per-variable views (flat slices) of one flat_step buffer."""
+    out, off = [], 0
+    for n in numels:
+        out.append(flat[off:off + n])
+        off += n
+    return out
 
 
 def normal_bf16(seed: int, numel: int, device="cpu", sigma: float = SIGMA) -> torch.Tensor:
