@@ -11,7 +11,7 @@ The native library (``lib/libddpb.so``, C ABI in ``include/ddpb.h``) does all
 of the work; this package only marshals arguments. Importing the package does
 not load the library; the first use does, and fails loudly if it was not built.
 """
-from ._abi import (DdpbError, Lib, lib, F32, BF16, MODE_FUSED, MODE_STAGED,  # noqa: F401
+from ._abi import (DdpbError, Lib, lib, F32, BF16, MODE_FUSED, MODE_STAGED, STATIC_SCRATCH_BYTES,  # noqa: F401
                    BIND_DEVICE_TIMESTAMPS, BIND_TIME_LAUNCHES, BIND_ROCTX, HIP_LIB, HOSTONLY_LIB, SYMBOLS,
                    OK, E_ARG, E_INDEX, E_DOUBLE_READY, E_INCOMPLETE, E_STATE, E_HIP, E_NOMEM)
 from .reducer import Reducer, StepTable  # noqa: F401
@@ -32,6 +32,6 @@ for _n in ["reducer_create", "destroy", "num_buckets", "get_locator", "get_bucke
            "get_launch_log", "get_launch_times", "device_clock_hz", "last_error", "set_launch_blocks",
            "set_workgroups_per_cu",
            "view_storage_elems", "get_view_offset", "bind_bucket_views", "rebuild_buckets", "get_ready_order",
-           "set_local_used", "set_sync_step"]:
+           "set_local_used", "set_sync_step", "bind_static"]:
     globals()[_n] = _fwd(_n)
 del _n

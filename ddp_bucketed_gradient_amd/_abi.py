@@ -18,6 +18,8 @@ F32, BF16 = 0, 1
 MODE_FUSED, MODE_STAGED = 0, 1
 BIND_DEVICE_TIMESTAMPS, BIND_TIME_LAUNCHES, BIND_ROCTX = 1, 2, 4
 
+STATIC_SCRATCH_BYTES = 32 << 20      # DDPB_STATIC_SCRATCH_BYTES
+
 OK, E_ARG, E_INDEX, E_DOUBLE_READY, E_INCOMPLETE, E_STATE, E_HIP, E_NOMEM = 0, -1, -2, -3, -4, -5, -6, -7
 _NAMES = {E_ARG: "E_ARG", E_INDEX: "E_INDEX", E_DOUBLE_READY: "E_DOUBLE_READY",
           E_INCOMPLETE: "E_INCOMPLETE", E_STATE: "E_STATE", E_HIP: "E_HIP", E_NOMEM: "E_NOMEM"}
@@ -31,7 +33,7 @@ SYMBOLS = [
     "ddpb_get_launch_times", "ddpb_device_clock_hz", "ddpb_last_error", "ddpb_set_launch_blocks",
     "ddpb_set_workgroups_per_cu", "ddpb_set_sync_step",
     "ddpb_view_storage_elems", "ddpb_get_view_offset", "ddpb_bind_bucket_views",
-    "ddpb_rebuild_buckets", "ddpb_get_ready_order", "ddpb_set_local_used",
+    "ddpb_rebuild_buckets", "ddpb_get_ready_order", "ddpb_set_local_used", "ddpb_bind_static",
 ]
 
 
@@ -62,6 +64,7 @@ def _sig(lib):
         "ddpb_get_segment": [vp, i32, P32, P32, P64, P64, P64],
         "ddpb_workspace_bytes": [vp, i32, P64],
         "ddpb_bind": [vp, C.POINTER(vp), vp, i64, vp, C.POINTER(vp), i32, i32, i32],
+        "ddpb_bind_static": [vp, C.POINTER(vp), vp, i32],
         "ddpb_ensure_prior_reduction_finished": [vp],
         "ddpb_mark_ready": [vp, i32],
         "ddpb_mark_ready_many": [vp, P32, i32],
@@ -167,6 +170,10 @@ class Lib:
         self._check(self.dll.ddpb_bind(h, gp, vp(int(workspace)) if workspace else None, int(ws_bytes),
                                        vp(int(compute_stream)) if compute_stream else None, ss,
                                        len(side_streams), mode, flags))
+
+    def bind_static(self, h, grad_ptrs: Sequence[int], compute_stream: int, mode: int):
+        gp = (vp * max(len(grad_ptrs), 1))(*[vp(int(p)) for p in grad_ptrs])
+        self._check(self.dll.ddpb_bind_static(h, gp, vp(int(compute_stream)) if compute_stream else None, mode))
 
     # -- iteration ------------------------------------------------------------------
     def ensure_prior_reduction_finished(self, h):

@@ -158,6 +158,24 @@ int ddpb_bind(ddpb_t h, void* const* grad_ptrs, void* workspace, int64_t ws_byte
   return pass(h->red.bind(a, &err), err);
 }
 
+int ddpb_bind_static(ddpb_t h, void* const* grad_ptrs, void* compute_stream, int32_t mode) {
+  if (!h) return fail(DDPB_E_ARG, "bind_static: NULL handle");
+  const ddpb::Plan& p = h->red.plan();
+  if (mode != DDPB_MODE_FUSED && mode != DDPB_MODE_STAGED) return fail(DDPB_E_ARG, "bind_static: bad mode");
+  const size_t n = static_cast<size_t>(p.R) * p.P;
+  if (n > 0 && grad_ptrs == nullptr) return fail(DDPB_E_ARG, "bind_static: grad_ptrs is NULL");
+  ddpb::BindArgs a;
+  a.grad_ptrs.assign(grad_ptrs, grad_ptrs + n);
+  for (size_t i = 0; i < n; ++i)
+    if (a.grad_ptrs[i] == nullptr && p.numel[i % p.P] > 0) return fail(DDPB_E_ARG, "bind_static: NULL gradient pointer");
+  a.compute_stream = compute_stream;
+  a.side_streams.assign(1, compute_stream);
+  a.mode = mode;
+  a.no_alloc = true;
+  std::string err;
+  return pass(h->red.bind(a, &err), err);
+}
+
 int ddpb_rebuild_buckets(ddpb_t h, int64_t bucket_cap_bytes) {
   if (!h) return fail(DDPB_E_ARG, "rebuild_buckets: NULL handle");
   std::string err;

@@ -42,6 +42,7 @@ int Reducer::bind(const BindArgs& args, std::string* err) {
     rc = launcher_->bind(plan_, args, err);
   }
   bound_ = (rc == kOk);
+  static_bind_ = bound_ && args.no_alloc;
   sync_step_set_ = false;          // the launcher's tables were released
   // The launch log and the timing history refer to the previous binding's
   // buckets and events: start both afresh.
@@ -135,6 +136,10 @@ int Reducer::mark_unused_ready(int32_t call, std::string* err) {
 }
 
 int Reducer::set_local_used(const uint8_t* used, std::string* err) {
+  if (static_bind_) {
+    *err = "set_local_used: a binding made by ddpb_bind_static has no staging for used flags";
+    return kErrState;
+  }
   if (iteration_open()) {
     *err = "set_local_used: must come before the iteration's hooks";
     return kErrState;
@@ -156,6 +161,10 @@ int Reducer::set_sync_step(void* const* step_ptrs, int32_t step_dtype, bool firs
   if (step_ptrs == nullptr || (step_dtype != 0 && step_dtype != 1)) {
     *err = "set_sync_step: bad step pointers or dtype";
     return kErrArg;
+  }
+  if (static_bind_) {
+    *err = "set_sync_step: a binding made by ddpb_bind_static has no staging for step tables";
+    return kErrState;
   }
   if (failed_) {
     *err = "the previous iteration left buckets unreduced; a new iteration cannot start before ddpb_reset";
@@ -248,6 +257,10 @@ int Reducer::accumulate(void* const* step_ptrs, int32_t step_dtype, bool first, 
     *err = "no_sync_accumulate: bad step pointers or dtype";
     return kErrArg;
   }
+  if (static_bind_) {
+    *err = "no_sync_accumulate: a binding made by ddpb_bind_static has no staging for step tables";
+    return kErrState;
+  }
   if (failed_) {
     *err = "the previous iteration left buckets unreduced; a new iteration cannot start before ddpb_reset";
     return kErrIncomplete;
@@ -277,6 +290,7 @@ int Reducer::rebuild_buckets(int64_t cap_bytes, std::string* err) {
   const std::vector<int32_t> order = last_order_;
   plan_ = make_plan(plan_.numel, plan_.elem_size, cap_bytes, plan_.R, &order);
   bound_ = false;                  // device tables and events follow the new plan at the next bind
+  static_bind_ = false;
   drop_sync_step();
   log_.clear();
   begin_iteration();

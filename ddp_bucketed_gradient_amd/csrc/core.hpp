@@ -98,7 +98,15 @@ struct BindArgs {
   std::vector<void*> side_streams;
   int32_t mode = 0;
   int32_t flags = 0;
+  // Allocation-free binding (ddpb_bind_static): the device tables and the
+  // staged workspace live in the library's static device array, the
+  // reductions run on the compute stream, and nothing is allocated.
+  bool no_alloc = false;
 };
+
+// Bytes of the static device array behind allocation-free bindings (one per
+// device, shared by every such binding on it).
+constexpr int64_t kStaticScratchBytes = int64_t(32) << 20;
 
 int64_t workspace_bytes(const Plan& plan, int32_t mode);
 
@@ -184,6 +192,7 @@ class Reducer {
   Plan plan_;
   std::unique_ptr<Launcher> launcher_;
   bool bound_ = false;
+  bool static_bind_ = false;       // bound by ddpb_bind_static: no staging for tables
   bool sync_ = true;
   bool failed_ = false;            // latched "prior reduction did not finish"
   std::vector<int32_t> pending_;   // per bucket

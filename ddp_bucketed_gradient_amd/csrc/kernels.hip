@@ -46,12 +46,47 @@
 #include <algorithm>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "core.hpp"
 
+// Device memory of the allocation-free bindings (ddpb_bind_static): their
+// pointer and segment tables and, in staged mode, their flat buckets. Every
+// device that loads the library holds one copy until the process ends. Host
+// code never uses this name as an address: the address of a device's copy
+// comes from hipGetSymbolAddress (static_scratch_base below).
+static __device__ __align__(256) unsigned char scratch[ddpb::kStaticScratchBytes];
+
 namespace ddpb {
 namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Per device: the address of its copy of `scratch` (looked up once, with the
+// device current) and the launcher whose tables it holds now.
+std::mutex g_scratch_mu;
+char* g_scratch_base[kMaxDevices] = {};
+const void* g_scratch_owner[kMaxDevices] = {};
+
+int static_scratch_base(int device, char** base, std::string* err) {
+  if (device < 0 || device >= kMaxDevices) {
+    *err = "bind_static: device ordinal out of range";
+    return kErrArg;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_base[device] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      *err = std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e);
+      return kErrHip;
+    }
+    g_scratch_base[device] = static_cast<char*>(p);
+  }
+  *base = g_scratch_base[device];
+  return kOk;
+}
 
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlock = 64 * kWavesPerBlock;
@@ -871,6 +906,7 @@ class HipLauncher final : public Launcher {
 
   int bind(const Plan& plan, const BindArgs& a, std::string* err) override {
     release();
+    if (a.no_alloc) return bind_static(plan, a, err);
     plan_ = &plan;
     R_ = plan.R;
     P_ = plan.P;
@@ -963,6 +999,10 @@ class HipLauncher final : public Launcher {
   }
 
   int launch(int32_t first, int32_t last, int64_t iteration, std::string* err) override {
+    if (static_ && !owns_scratch()) {
+      *err = "launch: another handle's ddpb_bind_static has taken over this device's static tables; bind again";
+      return kErrState;
+    }
     char what[48] = "";
     if (flags_ & 4) std::snprintf(what, sizeof(what), "ddpb launch %d-%d", first, last);
     const HostRange range((flags_ & 4) != 0, what);
@@ -1014,6 +1054,10 @@ class HipLauncher final : public Launcher {
 
   int accumulate(void* const* step_ptrs, int32_t step_dtype, bool first, std::string* err) override {
     const HostRange range((flags_ & 4) != 0, "ddpb no_sync_accumulate");
+    if (static_) {
+      *err = "no_sync_accumulate: not available on a binding made by ddpb_bind_static";
+      return kErrState;
+    }
     const size_t nptr = static_cast<size_t>(R_) * P_;
     if (plan_->segs.empty()) return kOk;
     bool cap = false;
@@ -1067,7 +1111,8 @@ class HipLauncher final : public Launcher {
                   std::string* err) override {
     const size_t B = static_cast<size_t>(plan_->B());
     std::vector<int64_t> h(std::max<size_t>(B, 1) * 4, 0);
-    HIP_OK(hipMemcpy(h.data(), d_stamps_, h.size() * sizeof(int64_t), hipMemcpyDeviceToHost), "read stamps");
+    if (d_stamps_ != nullptr)        // (a static binding keeps no stamps)
+      HIP_OK(hipMemcpy(h.data(), d_stamps_, h.size() * sizeof(int64_t), hipMemcpyDeviceToHost), "read stamps");
     t0->resize(log.size());
     t1->resize(log.size());
     for (size_t i = 0; i < log.size(); ++i) {
@@ -1110,6 +1155,10 @@ class HipLauncher final : public Launcher {
       used_active_ = false;
       return kOk;
     }
+    if (static_) {
+      *err = "used flags are not available on a binding made by ddpb_bind_static";
+      return kErrState;
+    }
     const size_t n = static_cast<size_t>(R_) * P_;
     if (n == 0) return kOk;
     bool cap = false;
@@ -1132,6 +1181,10 @@ class HipLauncher final : public Launcher {
     if (step_ptrs == nullptr) {
       sync_step_active_ = false;
       return kOk;
+    }
+    if (static_) {
+      *err = "set_sync_step: not available on a binding made by ddpb_bind_static";
+      return kErrState;
     }
     const HostRange range((flags_ & 4) != 0, "ddpb set_sync_step");
     const size_t n = static_cast<size_t>(R_) * P_;
@@ -1164,6 +1217,74 @@ class HipLauncher final : public Launcher {
   }
 
  private:
+  // Allocation-free binding: the pointer and segment tables (and the staged
+  // mode's flat buckets) are placed in this device's copy of `scratch`; the
+  // reductions run on the compute stream, so no event is needed either.
+  // Calls no hipMalloc, hipHostMalloc or hipEventCreate.
+  int bind_static(const Plan& plan, const BindArgs& a, std::string* err) {
+    plan_ = &plan;
+    R_ = plan.R;
+    P_ = plan.P;
+    mode_ = a.mode;
+    flags_ = 0;
+    compute_ = static_cast<hipStream_t>(a.compute_stream);
+    side_.assign(1, compute_);
+    side_used_.assign(1, 0);
+    pow2_ = (R_ & (R_ - 1)) == 0;
+    scale_ = 1.0f / static_cast<float>(R_);
+    vec_ok_ = 1;
+    flat_ = nullptr;
+    avg_ = nullptr;
+    HIP_OK(hipGetDevice(&device_), "hipGetDevice");
+    char* base = nullptr;
+    if (const int rc = static_scratch_base(device_, &base, err); rc != kOk) return rc;
+    auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+    const int64_t nptr = static_cast<int64_t>(R_) * P_;
+    const int64_t off_segs = up(nptr * static_cast<int64_t>(sizeof(float*)));
+    const int64_t off_flat = off_segs + up(static_cast<int64_t>(plan.segs.size() * sizeof(Segment)));
+    const int64_t need = off_flat + (mode_ == kModeStaged ? workspace_bytes(plan, kModeStaged) : 0);
+    if (need > kStaticScratchBytes) {
+      *err = "bind_static: this model needs " + std::to_string(need) + " bytes of device tables" +
+             (mode_ == kModeStaged ? " and flat buckets" : "") + ", the static array holds " +
+             std::to_string(kStaticScratchBytes) + "; use ddpb_bind";
+      plan_ = nullptr;
+      return kErrArg;
+    }
+    const void* prev = nullptr;
+    {
+      std::lock_guard<std::mutex> lock(g_scratch_mu);
+      prev = g_scratch_owner[device_];
+      g_scratch_owner[device_] = this;
+    }
+    static_ = true;
+    // The previous holder's reductions may still read the tables: let the
+    // device drain before they are overwritten.
+    if (prev != nullptr && prev != this) HIP_OK(hipDeviceSynchronize(), "bind_static: synchronize");
+    d_grads_ = reinterpret_cast<float**>(base);
+    d_segs_ = reinterpret_cast<Segment*>(base + off_segs);
+    if (mode_ == kModeStaged) {
+      flat_ = reinterpret_cast<float*>(base + off_flat);
+      avg_ = flat_ + static_cast<int64_t>(R_) * plan.flat_elems;
+    }
+    // Every byte the kernels read is written here (tables) or by the pack
+    // kernel before the mean kernel reads it (flat buckets): nothing has to
+    // start at zero.
+    if (nptr)
+      HIP_OK(hipMemcpyAsync(d_grads_, a.grad_ptrs.data(), nptr * sizeof(float*), hipMemcpyHostToDevice, compute_),
+             "upload pointer table");
+    if (!plan.segs.empty())
+      HIP_OK(hipMemcpyAsync(d_segs_, plan.segs.data(), plan.segs.size() * sizeof(Segment), hipMemcpyHostToDevice,
+                            compute_),
+             "upload segment table");
+    HIP_OK(hipStreamSynchronize(compute_), "bind_static: synchronize");
+    return update_lds_reserve(err);
+  }
+
+  bool owns_scratch() const {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    return g_scratch_owner[device_] == this;
+  }
+
   int enqueue_bucket(int32_t b, hipStream_t s, hipEvent_t t0, hipEvent_t t1, std::string* err) {
     // Bucket-view mode runs the same fused kernel over the bucket's flat range
     // of each replica's storage (one pseudo-variable per replica). With used
@@ -1313,6 +1434,17 @@ class HipLauncher final : public Launcher {
   }
 
   void release() {
+    if (static_) {                 // the tables live in `scratch`: nothing to free
+      {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        if (g_scratch_owner[device_] == this) g_scratch_owner[device_] = nullptr;
+      }
+      static_ = false;
+      d_grads_ = nullptr;
+      d_segs_ = nullptr;
+      flat_ = nullptr;
+      avg_ = nullptr;
+    }
     for (auto e : ev_ready_) if (e) (void)hipEventDestroy(e);
     for (auto e : ev_done_) if (e) (void)hipEventDestroy(e);
     for (auto e : ev_slot_) if (e) (void)hipEventDestroy(e);
@@ -1356,6 +1488,7 @@ class HipLauncher final : public Launcher {
   }
 
   const Plan* plan_ = nullptr;
+  bool static_ = false;        // bound by bind_static: tables in `scratch`
   int32_t R_ = 0, P_ = 0, mode_ = 0, flags_ = 0;
   int device_ = 0;
   bool pow2_ = true;

@@ -89,6 +89,26 @@ class Reducer:
         self.lib.bind(self.h, ptrs, ws.data_ptr() if ws is not None else 0, nbytes, compute.cuda_stream,
                       [s.cuda_stream for s in sides], mode, flags)
 
+    def bind_static(self, grads, compute_stream=None, mode: int = MODE_FUSED):
+        """Allocation-free binding (ddpb_bind_static): the library's tables sit
+        in its static device array and the reductions run on the compute
+        stream; grads as for bind."""
+        import torch
+        if len(grads) != self.R or any(len(row) != self.P for row in grads):
+            raise ValueError("grads must be R x P")
+        ptrs = []
+        for r in range(self.R):
+            for v in range(self.P):
+                t = grads[r][v]
+                n = self._numel[v]
+                if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or t.numel() != n:
+                    raise ValueError(f"grads[{r}][{v}] must be a contiguous fp32 CUDA tensor of {n} elements")
+                ptrs.append(t.data_ptr())
+        compute = compute_stream if compute_stream is not None else torch.cuda.current_stream()
+        self._keep = [grads, compute]
+        self.compute_stream, self.side_streams, self.workspace = compute, [compute], None
+        self.lib.bind_static(self.h, ptrs, compute.cuda_stream, mode)
+
     def bind_bucket_views(self, device=None, compute_stream=None, side_streams=None, flags: int = 0):
         """gradient_as_bucket_view: allocate one flat fp32 storage per replica
         in bucket layout (all R in one allocation), bind them, and return R x P

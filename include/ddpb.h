@@ -151,6 +151,31 @@ int ddpb_bind(ddpb_t h, void* const* grad_ptrs, void* workspace, int64_t ws_byte
               void* compute_stream, void* const* side_streams, int32_t n_side,
               int32_t mode, int32_t flags);
 
+/* Binding for callers that cannot allocate device memory: code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc. Same as ddpb_bind (grad_ptrs, compute_stream and mode mean the
+ * same) except that the library allocates nothing: its pointer and segment
+ * tables and, in DDPB_MODE_STAGED, its flat buckets (no workspace argument)
+ * are placed in a static device array of DDPB_STATIC_SCRATCH_BYTES bytes
+ * that every device the library runs on holds until the process ends. No
+ * hipMalloc, hipHostMalloc or hipEventCreate is called; the bucket reductions
+ * run on the compute stream itself (no side streams, no events, no flags).
+ * Needs round256(R*P*8) + round256(segments*32) bytes (ddpb_num_segments),
+ * plus ddpb_workspace_bytes(STAGED) in staged mode; a larger model gets
+ * DDPB_E_ARG and is left unbound.
+ * The array is shared by every static binding on a device and keeps the last
+ * binding's tables: a later ddpb_bind_static on the same device waits for the
+ * device to drain and takes the array over, after which the earlier handle's
+ * launches fail with DDPB_E_STATE until it is bound again. Static bindings of
+ * one device used from several threads at once race. Nothing in the array
+ * needs to start at zero (every byte the kernels read is written first).
+ * ddpb_no_sync_accumulate, ddpb_set_sync_step and ddpb_set_local_used need
+ * pinned staging that only ddpb_bind allocates and return DDPB_E_STATE on a
+ * static binding. Errors: DDPB_E_ARG, DDPB_E_STATE (iteration in progress),
+ * DDPB_E_HIP. */
+enum { DDPB_STATIC_SCRATCH_BYTES = 32 << 20 };
+int ddpb_bind_static(ddpb_t h, void* const* grad_ptrs, void* compute_stream, int32_t mode);
+
 /* Ready-order bucket rebuild ([C30] "第一次迭代为何不同"): re-plans the buckets
  * from the order in which the hooks fired in the last finished iteration,
  * first-ready variable first, with the same rule (whole tensors, the bucket

@@ -482,3 +482,30 @@ def test_reset_drops_used_flags(host):
     red.sync([1, 0])
     orc.sync([1, 0])
     assert red.launch_log() == orc.launch_log[-2:] == [(0, 0), (1, 1)]
+
+
+def test_static_binding_arguments_and_refusals(host):
+    """ddpb_bind_static: bad mode and NULL gradient pointers are refused before
+    anything is bound; on a static binding the calls that need pinned staging
+    (accumulation, synchronising step, used flags) are refused, syncs run; a
+    later ddpb_bind lifts the refusals."""
+    red = _reducer(host, [4, 6], 2, 0)
+    ptrs = [0x1000 + 64 * i for i in range(4)]
+    with pytest.raises(D.DdpbError) as e:
+        host.bind_static(red.h, ptrs, 0, 7)
+    assert e.value.code == _abi.E_ARG
+    with pytest.raises(D.DdpbError) as e:
+        host.bind_static(red.h, ptrs[:3] + [0], 0, D.MODE_FUSED)
+    assert e.value.code == _abi.E_ARG
+    host.bind_static(red.h, ptrs, 0, D.MODE_STAGED)
+    fake = _abi.ptr_array([0x5000 + 64 * i for i in range(4)])
+    for call in (lambda: host.no_sync_accumulate(red.h, fake, D.F32, True),
+                 lambda: host.set_sync_step(red.h, fake, D.F32, False),
+                 lambda: host.set_local_used(red.h, [1, 1, 1, 0])):
+        with pytest.raises(D.DdpbError) as e:
+            call()
+        assert e.value.code == _abi.E_STATE
+    red.sync()
+    assert red.launch_log() == [(0, 0), (1, 1)]
+    _bind_fake(red)
+    host.no_sync_accumulate(red.h, fake, D.F32, True)
