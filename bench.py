@@ -26,7 +26,6 @@ flags), ``--wg-per-cu`` (reduction workgroups per compute unit).
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import re
@@ -74,10 +73,20 @@ def parse():
                     help="reduction workgroups per compute unit (0 = no limit); default the "
                          "library's (1), and for --config 5 a sweep of 1 and 0")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="configs 2/3/6: skip the product-native ceiling (the same tensors at R = 1)")
+    ap.add_argument("--first-on-compute", action="store_true",
+                    help="configs 2/3/6: the compute stream itself comes first in the side-stream list, "
+                         "so bucket 0 (and every (n_side+1)-th) needs no cross-stream event")
     ap.add_argument("--roctx", action="store_true",
-                    help="configs 2/3/6: bind with DDPB_BIND_ROCTX (host-side ranges for rocprofv3 --marker-trace)")
+                    help="configs 2/3/6: bind with DDPB_BIND_ROCTX (host-side ranges for rocprofv3 "
+                         "--marker-trace); --config 5: a range around each timed phase")
     ap.add_argument("--cpu-sample-gb", type=float, default=24.0,
                     help="cap on the algorithmic bytes (2*R*S) of the oracle's sample")
+    ap.add_argument("--nosync-sample-mib", type=float, default=30.0,
+                    help="--config 4: fp32 MiB per replica of the oracle's sample (whole buckets, at least one)")
+    ap.add_argument("--overlap-sample-mib", type=float, default=256.0,
+                    help="--config 5: fp32 MiB per replica of the oracle's sample (whole buckets, at least one)")
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0,
                     help="the oracle repeats the sample's sync until this much CPU time")
     ap.add_argument("--no-time-launches", action="store_true",
@@ -100,15 +109,23 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_hash() -> str:
-    """sha256 prefix of the sources that decide what the kernels read and
-    write: the kernels and their launcher, the segment planner and the
-    descriptor layout they share (not the readiness state machine)."""
-    h = hashlib.sha256()
-    for name in ("kernels.hip", "core.hpp", "plan.cpp"):
-        with open(os.path.join(ROOT, "ddp_bucketed_gradient_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+from ddp_bucketed_gradient_amd.profiling import kernel_source_hash, union_length  # noqa: E402
+
+
+def overlap_from_profiles(workload: str, setting: str):
+    """The timeline figure of a --config 5 phase (share of the reduction
+    kernels' time concurrent with backward kernels) from the kernel and
+    marker trace summarised under profiles/; only while the kernel sources
+    are unchanged."""
+    p = os.path.join(ROOT, "profiles", "overlap.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        e = json.load(f).get(workload)
+    if not e or e.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    ph = e["phases"].get(setting)
+    return dict(ph, profile=e["profile"]) if ph else None
 
 
 def traffic_from_profiles(kernel: str, workload: str):
@@ -125,29 +142,14 @@ def traffic_from_profiles(kernel: str, workload: str):
     return e.get("bytes_per_launch")
 
 
-def union_length(starts, durs) -> float:
-    """Length of the union of the intervals [s, s + d)."""
-    iv = sorted(zip(starts, durs))
-    total, cur_s, cur_e = 0.0, None, None
-    for s, d in iv:
-        e = s + d
-        if cur_e is None or s > cur_e:
-            if cur_e is not None:
-                total += cur_e - cur_s
-            cur_s, cur_e = s, e
-        else:
-            cur_e = max(cur_e, e)
-    if cur_e is not None:
-        total += cur_e - cur_s
-    return total
+COPY_BYTES = 4_000_000_000
 
 
-COPY_CEILING_BYTES = 4_000_000_000
-
-
-def hbm_copy_ceiling(torch, nbytes: int = COPY_CEILING_BYTES) -> float:
-    """Plain device-to-device copy bandwidth of nbytes (read + write bytes /
-    time), the practical ceiling the sync is also compared with."""
+def torch_copy_GBps(torch, nbytes: int = COPY_BYTES) -> float:
+    """Bandwidth of torch's device-to-device copy of nbytes (read + write
+    bytes / time; the runtime's blit kernel). Context only: a hand-written
+    streaming kernel beats it, so it is no ceiling. Its 4 GB dispatches also
+    calibrate the HBM byte counters of a rocprofv3 --pmc run of the bench."""
     n = nbytes // 4
     a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
     b = torch.empty_like(a)
@@ -250,6 +252,86 @@ def sync_workload(args, WC):
     return w
 
 
+def time_syncs(torch, red, run_step, steps, compute, timed_launches):
+    """Times `steps` calls of run_step (one whole sync each) on the compute
+    stream: wall clock between two device synchronisations, one event per
+    sync boundary (median and p95), host time inside the calls, and -- with
+    per-launch events -- the union of each sync's launch intervals."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    per_step = []                       # (starts, durations) of every launch, per step
+    ring = 64                           # iterations whose launch events the library keeps
+    read = 0                            # timed steps whose launch times were collected
+    torch.cuda.synchronize()            # barrier (one process) + device sync
+    t0 = time.perf_counter()
+    host_s = 0.0
+    evs[0].record(compute)
+    for k in range(steps):
+        h0 = time.perf_counter()
+        run_step()
+        host_s += time.perf_counter() - h0
+        evs[k + 1].record(compute)
+        # Collect launch times of steps that are about to leave the library's
+        # ring, well behind the device, so the host never waits on recent work.
+        while timed_launches and k - read >= ring - 8:
+            per_step.append(red.launch_times_ms(k - read, True))
+            read += 1
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    while timed_launches and read < steps:
+        per_step.append(red.launch_times_ms(steps - 1 - read, True))
+        read += 1
+    sync_ms = sorted(evs[k].elapsed_time(evs[k + 1]) for k in range(steps))
+    half = len(sync_ms) // 2
+    return {"wall_ms": (t1 - t0) * 1e3 / steps,
+            "ev_ms": evs[0].elapsed_time(evs[-1]) / steps,
+            "med_ms": sync_ms[half] if len(sync_ms) % 2 else 0.5 * (sync_ms[half - 1] + sync_ms[half]),
+            "p95_ms": sync_ms[-(-95 * len(sync_ms) // 100) - 1],            # nearest rank
+            "host_s": host_s,
+            "launch_ms": [d for _, ds in per_step for d in ds],
+            "busy_ms": sum(union_length(st, ds) for st, ds in per_step)}
+
+
+def product_ceiling(torch, D, grads, numels, R, cap, compute, sides, steps, warmup):
+    """The practical ceiling of an in-place pass over the same bytes with the
+    product's own kernel: every replica's tensor of every variable becomes a
+    variable of one reducer with R = 1 (the mean of one replica is the
+    replica, so each element is read once and written back once, the sync's
+    1:1 mix with one stream per wave instead of R), numbered variable-major so
+    that reverse order visits the R copies of each variable together, under R
+    times the cap, so its buckets hold what the R-replica buckets hold. Same
+    streams and launch timing; all hooks in one call. The best of one
+    workgroup per CU and no limit."""
+    P = len(numels)
+    shapes = [(numels[v],) for v in range(P) for _ in range(R)]
+    flat = [[grads[r][v].view(-1) for v in range(P) for r in range(R)]]
+    order = list(range(P * R))[::-1]
+    red = D.Reducer(shapes, 1, cap * R)
+    red.bind(flat, compute_stream=compute, side_streams=sides, flags=D.BIND_TIME_LAUNCHES)
+    # all hooks in one call: R times as many variables would otherwise make
+    # the Python hook loop, not the device, the bottleneck
+    def one():
+        red.mark_ready_many(order)
+        red.finalize()
+
+    best = None
+    for wg in (1, 0):
+        red.set_workgroups_per_cu(wg)
+        for _ in range(warmup):
+            one()
+        t = time_syncs(torch, red, one, steps, compute, True)
+        if best is None or t["wall_ms"] < best[1]["wall_ms"]:
+            best = (wg, t)
+    wg, t = best
+    alg = 2 * R * 4 * sum(numels)
+    out = {"GBps": round(alg / (t["wall_ms"] * 1e-3) / 1e9, 1), "ms_per_sync": round(t["wall_ms"], 4),
+           "GBps_union": round(alg * steps / (t["busy_ms"] * 1e-3) / 1e9, 1),
+           "buckets": red.num_buckets, "workgroups_per_cu": wg,
+           "what": f"fused_mean_kernel at R = 1 over the same {R} x {P} tensors (in place, each byte read "
+                   f"once and written once), cap {R} x the sync's, same side streams, hooks in one call"}
+    red.close()
+    return out
+
+
 def run_sync_bench(args, torch, D, WG, WC):
     w = sync_workload(args, WC)
     params = w.params()
@@ -261,7 +343,8 @@ def run_sync_bench(args, torch, D, WG, WC):
 
     red = D.Reducer([p.shape for p in params], R, w.cap_bytes)
     B = red.num_buckets
-    flags = 0 if (args.no_time_launches or args.graph) else D.BIND_TIME_LAUNCHES
+    timed_launches = not (args.no_time_launches or args.graph)
+    flags = D.BIND_TIME_LAUNCHES if timed_launches else 0
     if args.roctx:
         flags |= D.BIND_ROCTX
     # The compute stream and the side streams are consecutive streams of
@@ -269,6 +352,8 @@ def run_sync_bench(args, torch, D, WG, WC):
     # (it hands out its 4 queues round-robin); the legacy null stream stays idle.
     compute = torch.cuda.Stream()
     sides = [torch.cuda.Stream() for _ in range(args.n_side)] if args.n_side > 0 else [compute]
+    if args.first_on_compute and args.n_side > 0:
+        sides = [compute] + sides        # bucket 0 (and every n_side+1-th) runs on the compute stream
     torch.cuda.set_stream(compute)
     if args.mode == "view":        # gradient_as_bucket_view: gradients are views of flat storages
         views = red.bind_bucket_views(compute_stream=compute, side_streams=sides, flags=flags)
@@ -343,41 +428,9 @@ def run_sync_bench(args, torch, D, WG, WC):
         torch.cuda.synchronize()
         log("captured one sync into a graph")
 
-    # one event on the compute stream before each sync and after the last: the
-    # interval between consecutive events is one sync (from the previous join
-    # to this sync's join), for the median and p95
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    per_step = []                       # (starts, durations) of every launch, per step
-    ring = 64                           # iterations whose launch events the library keeps
-    read = 0                            # timed steps whose launch times were collected
-    torch.cuda.synchronize()            # barrier (one process) + device sync
-    t0 = time.perf_counter()
-    host_s = 0.0                        # host time inside the hooks and finalize
-    evs[0].record(compute)
-    for k in range(args.steps):
-        h0 = time.perf_counter()
-        run_step()
-        host_s += time.perf_counter() - h0
-        evs[k + 1].record(compute)
-        # Collect launch times of steps that are about to leave the library's
-        # ring, well behind the device, so the host never waits on recent work.
-        while flags and k - read >= ring - 8:
-            per_step.append(red.launch_times_ms(k - read, True))
-            read += 1
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    while flags and read < args.steps:
-        per_step.append(red.launch_times_ms(args.steps - 1 - read, True))
-        read += 1
-    launch_ms = [d for _, ds in per_step for d in ds]
-    busy_ms = sum(union_length(st, ds) for st, ds in per_step)
-    wall_ms = (t1 - t0) * 1e3 / args.steps
-    ev_ms = evs[0].elapsed_time(evs[-1]) / args.steps
-    sync_ms = sorted(evs[k].elapsed_time(evs[k + 1]) for k in range(args.steps))
-    half = len(sync_ms) // 2
-    med_ms = sync_ms[half] if len(sync_ms) % 2 else 0.5 * (sync_ms[half - 1] + sync_ms[half])
-    p95_ms = sync_ms[-(-95 * len(sync_ms) // 100) - 1]      # nearest rank
-    log(f"timed {args.steps} steps: {wall_ms:.3f} ms/step wall, {ev_ms:.3f} ms/step events")
+    t = time_syncs(torch, red, run_step, args.steps, compute, timed_launches)
+    wall_ms, launch_ms, busy_ms = t["wall_ms"], t["launch_ms"], t["busy_ms"]
+    log(f"timed {args.steps} steps: {wall_ms:.3f} ms/step wall, {t['ev_ms']:.3f} ms/step events")
 
     alg = 2 * R * S
     if used is not None:
@@ -394,16 +447,25 @@ def run_sync_bench(args, torch, D, WG, WC):
         assert n_launch == B * args.steps, (n_launch, B, args.steps)
         avg_ms = sum(launch_ms) / n_launch
         bytes_per_launch = alg / B
-        # With one side stream the launches never overlap and busy time is the
-        # sum of launch durations; with several, launches on different streams
-        # run concurrently and the union of their intervals is the time the
-        # kernel occupied the GPU.
+        # Three bases for the kernel's rate. With one side stream the launches
+        # never overlap and the union of their intervals is the sum of their
+        # durations; with several, consecutive launches run concurrently, so
+        # the union is the time the kernel occupied the GPU (`achieved`), each
+        # launch's own duration is stretched by its neighbour (per launch), and
+        # the wall clock adds the gaps between syncs.
         achieved = alg * args.steps / (busy_ms * 1e-3) / 1e9
+        per_launch = bytes_per_launch / (avg_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
                     # stored counters cover every variable used by every replica
                     "traffic": traffic_from_profiles(kernel, w.name) if used is None else None,
-                    "kernel": kernel, "launches": n_launch, "avg_launch_us": round(avg_ms * 1e3, 2),
+                    "kernel": kernel,
+                    "basis": "union of each sync's launch intervals (HIP events on the dispatches, "
+                             "side streams)",
+                    "frac_union": round(achieved / HBM_PEAK_GBPS, 4),
+                    "frac_per_launch": round(per_launch / HBM_PEAK_GBPS, 4),
+                    "frac_wall": round(value / HBM_PEAK_GBPS, 4),
+                    "launches": n_launch, "avg_launch_us": round(avg_ms * 1e3, 2),
                     "alg_bytes_per_launch": bytes_per_launch,
                     "busy_us_per_step": round(busy_ms * 1e3 / args.steps, 2),
                     "launch_concurrency": round(sum(launch_ms) / busy_ms, 3)}
@@ -424,7 +486,12 @@ def run_sync_bench(args, torch, D, WG, WC):
                                      f"at least {reps_t} sync(s) each in {dt_t:.1f} s"}
         del host_in
 
-    copy_gbps = hbm_copy_ceiling(torch)
+    ceiling = None
+    if not args.no_ceiling and used is None and not args.graph:
+        log("product ceiling: the same tensors at R = 1")
+        ceiling = product_ceiling(torch, D, grads, numels, R, w.cap_bytes, compute, sides, args.steps,
+                                  max(1, args.warmup))
+    copy_gbps = torch_copy_GBps(torch)
     out = {
         "metric": "grad-sync GB/s and % HBM peak; ms per bucketed sync, BERT-large R=8"
         if w.cfg == 3 and R == 8 else f"grad-sync GB/s; ms per bucketed sync, {w.name}",
@@ -441,17 +508,20 @@ def run_sync_bench(args, torch, D, WG, WC):
         "data": "synthetic",
         "config": {"workload": w.name, "tensors": P, "params": sum(numels), "replicas": R,
                    "bucket_cap_bytes": w.cap_bytes, "buckets": B, "mode": args.mode,
-                   "side_streams": args.n_side, "hooks": args.hooks, "graph": args.graph,
+                   "side_streams": args.n_side, "first_bucket_on_compute_stream": bool(args.first_on_compute),
+                   "hooks": args.hooks, "graph": args.graph,
                    "unused_frac": args.unused_frac, "workgroups_per_cu": wg_per_cu,
+                   "launch_timing_events": timed_launches,
                    "alg_bytes_per_step": alg},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
-        "hbm_copy_GBps": round(copy_gbps, 1),
-        "pct_of_copy_ceiling": round(100 * value / copy_gbps, 2),
-        "ms_per_step_events": round(ev_ms, 4),
-        "ms_per_sync_median": round(med_ms, 4),
-        "ms_per_sync_p95": round(p95_ms, 4),
-        "host_ms_per_step": round(host_s * 1e3 / args.steps, 4),
-        "host_us_per_hook": round(host_s * 1e6 / (args.steps * P), 3),
+        "ceiling": ceiling,
+        "pct_of_ceiling": round(100 * value / ceiling["GBps"], 2) if ceiling else None,
+        "torch_copy_GBps": round(copy_gbps, 1),
+        "ms_per_step_events": round(t["ev_ms"], 4),
+        "ms_per_sync_median": round(t["med_ms"], 4),
+        "ms_per_sync_p95": round(t["p95_ms"], 4),
+        "host_ms_per_step": round(t["host_s"] * 1e3 / args.steps, 4),
+        "host_us_per_hook": round(t["host_s"] * 1e6 / (args.steps * P), 3),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "cpu_baseline_threads": cpu_threads,
@@ -466,6 +536,62 @@ def _pool_streams(torch, n_side):
     return compute, sides
 
 
+def time_oracle_threads(make_unit, groups, min_seconds):
+    """Runs make_unit(group)() repeatedly in one thread per group (NumPy
+    releases the GIL inside its array operations) for about min_seconds; the
+    unit returns its algorithmic bytes. Returns GB/s, seconds, the least
+    number of units any thread finished."""
+    import threading
+    units = [make_unit(g) for g in groups]
+    for u in units:
+        u()                          # untimed: first touch of the oracle's buffers
+    done = [0] * len(units)
+    reps = [0] * len(units)
+    stop = threading.Event()
+
+    def work(i):
+        while not stop.is_set():
+            done[i] += units[i]()
+            reps[i] += 1
+
+    ths = [threading.Thread(target=work, args=(i,)) for i in range(len(units))]
+    t0 = time.perf_counter()
+    for th in ths:
+        th.start()
+    if len(ths) == 1:
+        while time.perf_counter() - t0 < min_seconds and reps[0] == 0:
+            time.sleep(0.01)
+    time.sleep(max(0.0, min_seconds - (time.perf_counter() - t0)))
+    stop.set()
+    for th in ths:
+        th.join()
+    dt = time.perf_counter() - t0
+    return sum(done) / dt / 1e9, dt, min(reps)
+
+
+def nosync_oracle_unit(numels_s, R, k, cap, host_steps):
+    """One optimizer step of config 4 in the oracle, on the sample's variables:
+    k bf16 micro-steps accumulated in fp32 (the first assigns), then the
+    bucketed sync. host_steps[t][r][j]: uint16 bf16 bits of variable j."""
+    import numpy as np
+    from oracle import reducer as OR
+    orc = OR.Reducer(numels_s, R, cap)
+    acc = [[np.zeros(n, np.float32) for n in numels_s] for _ in range(R)]
+    orc.bind(acc)
+    N = sum(numels_s)
+    nbytes = R * N * (6 + 10 * (k - 1)) + 2 * R * 4 * N
+
+    def unit():
+        orc.set_sync(False)
+        for t in range(k):
+            if t == k - 1:
+                orc.set_sync(True)
+            orc.no_sync_accumulate(host_steps[t], first=(t == 0))
+        orc.sync()
+        return nbytes
+    return unit
+
+
 def run_nosync_bench(args, torch, D, WG, WC):
     """One step = k micro-steps: k-1 local backward passes accumulate under
     no_sync, the k-th accumulates with sync on and runs the bucketed sync."""
@@ -476,8 +602,10 @@ def run_nosync_bench(args, torch, D, WG, WC):
     S = 4 * N
     log(f"workload {w.name}: P={P} R={R} k={k} N={N}")
     grads = [[torch.zeros(n, dtype=torch.float32, device="cuda") for n in numels] for _ in range(R)]
-    steps = [[[WG.normal(WG.seed_of(4, r, v, t), n, "cuda").to(torch.bfloat16) for v, n in enumerate(numels)]
-              for r in range(R)] for t in range(k)]
+    # each replica's step gradients of one micro-step are one flat bf16 draw
+    # (three dispatches), the variables views into it
+    flats = [[WG.flat_step(4, r, t, N, "cuda") for r in range(R)] for t in range(k)]
+    steps = [[WG.flat_views(flats[t][r], numels) for r in range(R)] for t in range(k)]
     torch.cuda.synchronize()
     log("inputs generated on the device")
     compute, sides = _pool_streams(torch, args.n_side)
@@ -493,7 +621,7 @@ def run_nosync_bench(args, torch, D, WG, WC):
     step_args = steps if args.step_lists else [red.step_table(steps[t]) for t in range(k)]
     host_s = []
 
-    def one_step(timed):
+    def one_step(timed, n):
         h0 = time.perf_counter()
         for t in range(k):
             if t == k - 1:
@@ -509,23 +637,26 @@ def run_nosync_bench(args, torch, D, WG, WC):
             red.no_sync_accumulate(step_args[t], first_step=(t == 0))
             if timed:
                 e1.record(compute)
-                acc_ms.append((t, e0, e1))
+                acc_ms.append((n, t, e0, e1))
             red.sync(order)                    # hooks: no-ops until the last micro-step
         red.set_sync(False)
         if timed:
             host_s.append(time.perf_counter() - h0)
 
     red.set_sync(False)
-    for _ in range(args.warmup):
-        one_step(False)
+    for i in range(args.warmup):
+        one_step(False, i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        one_step(True)
+    for i in range(args.steps):
+        one_step(True, i)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    acc_first = [a.elapsed_time(b) for t, a, b in acc_ms if t == 0]
-    acc_rest = [a.elapsed_time(b) for t, a, b in acc_ms if t > 0]
+    acc_first = [a.elapsed_time(b) for _, t, a, b in acc_ms if t == 0]
+    acc_rest = [a.elapsed_time(b) for _, t, a, b in acc_ms if t > 0]
+    # per optimizer step: the mean of its later micro-steps (a slow run shows here)
+    by_step = [round(sum(a.elapsed_time(b) for n2, t, a, b in acc_ms if n2 == n and t > 0) /
+                     max(1, sum(1 for n2, t, _, _ in acc_ms if n2 == n and t > 0)), 4) for n in range(args.steps)]
     # the last sync's launches overlap on the side streams: their union is
     # the time the reduction occupied the GPU
     st, ds = red.launch_times_ms(0, True)
@@ -537,6 +668,45 @@ def run_nosync_bench(args, torch, D, WG, WC):
     avg_rest = sum(acc_rest) / len(acc_rest)
     bytes_rest = 10 * R * N
     achieved = bytes_rest / (avg_rest * 1e-3) / 1e9
+    sync_kernel = "fused_acc_mean_kernel<bf16,add>" if args.fused_last_step else "fused_mean_kernel"
+    sync_bytes = 10 * R * N if args.fused_last_step else 2 * R * S
+
+    cpu = cpu_threads = None
+    if not args.no_cpu_baseline:
+        # the oracle on the first buckets' variables (the last-defined ones),
+        # from the same device inputs
+        budget = args.nosync_sample_mib * MiB
+        nvars, sb = 0, 0
+        for b in range(red.num_buckets):
+            vars_b, nb = red.lib.get_bucket(red.h, b)
+            if sb > 0 and sb + nb > budget:
+                break
+            sb += nb
+            nvars += len(vars_b)
+        vs = list(range(P - nvars, P))
+        numels_s = [numels[v] for v in vs]
+        log(f"oracle sample: {nvars} tensors, {sb / 1e6:.1f} MB per replica (fp32), R={R}, k={k}")
+        host = [[[steps[t][r][v].view(torch.int16).cpu().numpy().view("uint16") for v in vs] for r in range(R)]
+                for t in range(k)]
+        gbs, dt, reps = time_oracle_threads(lambda g: nosync_oracle_unit(numels_s, R, k, w.cap_bytes, host),
+                                            [0], args.cpu_min_seconds)
+        cpu = {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{w.name}: first buckets ({nvars} tensors, {sb / 1e6:.1f} MB per replica) of the same "
+                         f"device inputs; {k} micro-steps accumulated and one bucketed sync per unit, on the "
+                         f"line's byte count; NumPy single thread, {reps} unit(s) in {dt:.1f} s"}
+        nthr = max(1, min(16, len(os.sched_getaffinity(0))))
+        if nthr > 1:
+            order_v = sorted(range(len(vs)), key=lambda j: -numels_s[j])
+            groups = [g for g in (order_v[i::nthr] for i in range(nthr)) if g]
+            gbs_t, dt_t, reps_t = time_oracle_threads(
+                lambda g: nosync_oracle_unit([numels_s[j] for j in g], R, k, w.cap_bytes,
+                                             [[[host[t][r][j] for j in g] for r in range(R)] for t in range(k)]),
+                groups, args.cpu_min_seconds)
+            cpu_threads = {"value": round(gbs_t, 3), "unit": "GB/s", "cores": len(groups), "kind": "oracle",
+                           "sample": f"same sample, its tensors dealt to {len(groups)} oracle reducers in threads; "
+                                     f"at least {reps_t} unit(s) each in {dt_t:.1f} s"}
+        del host
+    copy_gbps = torch_copy_GBps(torch)
     return {
         "metric": f"grad-sync GB/s; ms per optimizer step (k={k} no_sync micro-steps + 1 sync), {w.name}",
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -545,19 +715,27 @@ def run_nosync_bench(args, torch, D, WG, WC):
         "config": {"workload": w.name, "tensors": P, "params": N, "replicas": R, "micro_steps": k,
                    "step_dtype": "bf16", "buckets": red.num_buckets, "workgroups_per_cu": wg_per_cu,
                    "fused_last_step": args.fused_last_step, "step_tables": not args.step_lists,
-                   "alg_bytes_per_step": alg},
+                   "launch_timing_events": True, "alg_bytes_per_step": alg},
         "host_ms_per_step": round(1e3 * sum(host_s) / len(host_s), 4),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "accumulate_first_ms": round(sum(acc_first) / len(acc_first), 4),
-        "accumulate_ms": round(avg_rest, 4), "sync_busy_ms_last": round(sync_ms, 4),
+        "accumulate_ms": round(avg_rest, 4),
+        "accumulate_ms_by_step": by_step,
+        "accumulate_ms_min_max": [round(min(acc_rest), 4), round(max(acc_rest), 4)],
+        "sync_kernel": sync_kernel,
+        "sync_busy_ms_last": round(sync_ms, 4),
         # the fused last step reads the accumulators and the bf16 steps and writes the mean
-        "sync_busy_GBps_last": round((10 * R * N if args.fused_last_step else 2 * R * S) / (sync_ms * 1e-3) / 1e9, 1),
+        "sync_busy_GBps_last": round(sync_bytes / (sync_ms * 1e-3) / 1e9, 1),
+        "sync_traffic_bytes_per_launch": traffic_from_profiles(sync_kernel, w.name),
+        "torch_copy_GBps": round(copy_gbps, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic_from_profiles("accumulate_kernel<bf16,add>", w.name),
-                     "kernel": "accumulate_kernel<bf16,add>", "alg_bytes_per_launch": bytes_rest,
-                     "avg_launch_us": round(avg_rest * 1e3, 2)},
-        "cpu_baseline": None,
+                     "kernel": "accumulate_kernel<bf16,add>",
+                     "basis": "one launch per micro-step on the compute stream (events around it)",
+                     "alg_bytes_per_launch": bytes_rest, "avg_launch_us": round(avg_rest * 1e3, 2)},
+        "cpu_baseline": cpu,
+        "cpu_baseline_threads": cpu_threads,
     }
 
 
@@ -598,7 +776,10 @@ def run_overlap_bench(args, torch, D, WG, WC):
     shapes_def = [params[v].shape for v in perm]
     grads_def = [[row[v] for v in perm] for row in grads]
     red = D.Reducer(shapes_def, R, (1 << 62) if args.rebuild else cap)
-    red.bind(grads_def, compute_stream=compute, side_streams=sides, flags=D.BIND_TIME_LAUNCHES)
+    # DDPB_BIND_OVERLAP: the library's setting for a reduction beside a
+    # backward (no per-CU limit); the sweep below sets each value explicitly
+    bind_flags = D.BIND_TIME_LAUNCHES | D.BIND_OVERLAP
+    red.bind(grads_def, compute_stream=compute, side_streams=sides, flags=bind_flags)
     g0 = [grads[0][v].view(params[v].shape) for v in range(P)]
     order = [dpos[v] for v in w.ready_order()]
 
@@ -627,27 +808,30 @@ def run_overlap_bench(args, torch, D, WG, WC):
         backward(hook)
         red.finalize()
         red.rebuild_buckets(cap)
-        red.bind(grads_def, compute_stream=compute, side_streams=sides, flags=D.BIND_TIME_LAUNCHES)
+        red.bind(grads_def, compute_stream=compute, side_streams=sides, flags=bind_flags)
         torch.cuda.synchronize()
         log(f"rebuilt into {red.num_buckets} buckets from the recorded hook order")
 
-    def timed(fn, reps):
+    def timed(fn, reps, phase):
+        """ms per call of fn; with --roctx the timed calls sit in a host-side
+        range named after the phase, for a marker trace."""
         for _ in range(2):
             fn()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(compute)
-        for _ in range(reps):
-            fn()
-        e1.record(compute)
-        torch.cuda.synchronize()
+        with roctx_range(args.roctx, f"bench {phase}"):
+            e0.record(compute)
+            for _ in range(reps):
+                fn()
+            e1.record(compute)
+            torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
     def both():
         backward(hook)
         red.finalize()
 
-    t_bwd = timed(lambda: backward(none), args.steps)
+    t_bwd = timed(lambda: backward(none), args.steps, "backward alone")
     flops = 4 * 2 * T * d * f * L
     alg = 2 * R * S
     sweep = {}
@@ -659,8 +843,8 @@ def run_overlap_bench(args, torch, D, WG, WC):
         for mb in caps:
             red.set_workgroups_per_cu(wg)
             red.set_launch_blocks(mb)
-            t_red = timed(lambda: red.sync(order), args.steps)
-            t_both = timed(both, args.steps)
+            t_red = timed(lambda: red.sync(order), args.steps, f"reduction alone wg{wg} blocks{mb}")
+            t_both = timed(both, args.steps, f"both wg{wg} blocks{mb}")
             hidden = max(0.0, min(1.0, (t_bwd + t_red - t_both) / t_red))
             sweep[f"wg{wg}_blocks{mb}"] = {
                 "workgroups_per_cu": wg, "launch_blocks": mb,
@@ -675,7 +859,7 @@ def run_overlap_bench(args, torch, D, WG, WC):
     # with the best setting of the sweep.
     red.set_launch_blocks(0)
     red1 = D.Reducer(shapes_def, R, 1 << 62)
-    red1.bind(grads_def, compute_stream=compute, side_streams=sides, flags=D.BIND_TIME_LAUNCHES)
+    red1.bind(grads_def, compute_stream=compute, side_streams=sides, flags=bind_flags)
     red1.set_workgroups_per_cu(b["workgroups_per_cu"])
     red1.set_launch_blocks(b["launch_blocks"])
 
@@ -683,13 +867,56 @@ def run_overlap_bench(args, torch, D, WG, WC):
         backward(lambda v: red1.mark_ready(dpos[v]))
         red1.finalize()
 
-    t_red1 = timed(lambda: red1.sync(order), args.steps)
-    t_both1 = timed(both1, args.steps)
+    t_red1 = timed(lambda: red1.sync(order), args.steps, "control reduction alone")
+    t_both1 = timed(both1, args.steps, "control both")
     control = {"buckets": red1.num_buckets, "t_reduction_ms": round(t_red1, 4), "t_both_ms": round(t_both1, 4),
                "hidden": round(max(0.0, min(1.0, (t_bwd + t_red1 - t_both1) / t_red1)), 4)}
     log(f"single-bucket control: reduction {t_red1:.3f} ms alone, both {t_both1:.3f} ms, "
         f"hidden {control['hidden']:.3f}")
     red1.close()
+    cpu = cpu_threads = None
+    if not args.no_cpu_baseline:
+        # the oracle's sync (pack, fixed-order mean, copy-back) on the first
+        # buckets' variables, from the device's gradients as they now stand
+        import numpy as np
+        from oracle import reducer as OR
+        nvars, sb = 0, 0
+        for bb in range(red.num_buckets):
+            vars_b, nb = red.lib.get_bucket(red.h, bb)
+            if sb > 0 and sb + nb > args.overlap_sample_mib * MiB:
+                break
+            sb += nb
+            nvars += len(vars_b)
+        vs = list(range(P - nvars, P))           # reducer (definition-order) indices
+        host = [[grads_def[r][v].cpu().numpy().copy() for v in vs] for r in range(R)]
+        numels_s = [host[0][j].size for j in range(len(vs))]
+
+        def sync_unit(js):
+            orc = OR.Reducer([numels_s[j] for j in js], R, cap)
+            orc.bind([[np.array(host[r][j], copy=True) for j in js] for r in range(R)])
+            nbytes = 2 * R * 4 * sum(numels_s[j] for j in js)
+
+            def unit():
+                orc.sync()
+                return nbytes
+            return unit
+
+        log(f"oracle sample: {nvars} tensors, {sb / 1e6:.1f} MB per replica, R={R}")
+        gbs, dt, reps = time_oracle_threads(sync_unit, [list(range(len(vs)))], args.cpu_min_seconds)
+        cpu = {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{w.name}: first {nvars} tensors ({sb / 1e6:.1f} MB per replica, R={R}) of the "
+                         f"same gradients; the bucketed sync (pack, mean, copy-back) on the line's 2*R*S "
+                         f"numerator, to set beside reduction_GBps; NumPy single thread, {reps} sync(s) in "
+                         f"{dt:.1f} s"}
+        nthr = max(1, min(16, len(os.sched_getaffinity(0))))
+        if nthr > 1:
+            order_v = sorted(range(len(vs)), key=lambda j: -numels_s[j])
+            groups = [g for g in (order_v[i::nthr] for i in range(nthr)) if g]
+            gbs_t, dt_t, reps_t = time_oracle_threads(sync_unit, groups, args.cpu_min_seconds)
+            cpu_threads = {"value": round(gbs_t, 3), "unit": "GB/s", "cores": len(groups), "kind": "oracle",
+                           "sample": f"same sample, its tensors dealt to {len(groups)} oracle reducers in "
+                                     f"threads; at least {reps_t} sync(s) each in {dt_t:.1f} s"}
+        del host
     return {
         "metric": f"fraction of reduction hidden under backward; ms per step, {w.name}",
         "value": b["hidden"], "unit": "fraction", "n_gpus": 1, "steps": args.steps, "warmup": 2,
@@ -704,8 +931,38 @@ def run_overlap_bench(args, torch, D, WG, WC):
         "reduction_GBps": round(alg / (b["t_reduction_ms"] * 1e-3) / 1e9, 1),
         "sweep": sweep,
         "single_bucket_control": control,
-        "roofline": None, "cpu_baseline": None,
+        # rocprofv3 timeline of the same workload (kernel intervals inside the
+        # phase's marker range), stored under profiles/
+        "timeline": {"best": overlap_from_profiles(w.name, best), "control": overlap_from_profiles(w.name, "control")}
+        if not (args.shuffle_params or args.rebuild or args.cap_mib is not None) else None,
+        "roofline": None, "cpu_baseline": cpu, "cpu_baseline_threads": cpu_threads,
     }
+
+
+_ROCTX = None
+
+
+class roctx_range:
+    """A host-side roctx range (rocprofv3 --marker-trace) when `on`, through
+    the same roctx library the native code links."""
+
+    def __init__(self, on: bool, name: str):
+        self.on, self.name = on, name
+
+    def __enter__(self):
+        global _ROCTX
+        if self.on:
+            if _ROCTX is None:
+                import ctypes
+                _ROCTX = ctypes.CDLL("/opt/rocm/lib/librocprofiler-sdk-roctx.so.1")
+                _ROCTX.roctxRangePushA.argtypes = [ctypes.c_char_p]
+            _ROCTX.roctxRangePushA(self.name.encode())
+        return self
+
+    def __exit__(self, *exc):
+        if self.on:
+            _ROCTX.roctxRangePop()
+        return False
 
 
 def run_latency_bench(args, torch, D, WG, WC):

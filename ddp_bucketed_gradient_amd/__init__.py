@@ -12,7 +12,7 @@ of the work; this package only marshals arguments. Importing the package does
 not load the library; the first use does, and fails loudly if it was not built.
 """
 from ._abi import (DdpbError, Lib, lib, F32, BF16, MODE_FUSED, MODE_STAGED, STATIC_SCRATCH_BYTES,  # noqa: F401
-                   BIND_DEVICE_TIMESTAMPS, BIND_TIME_LAUNCHES, BIND_ROCTX, HIP_LIB, HOSTONLY_LIB, SYMBOLS,
+                   BIND_DEVICE_TIMESTAMPS, BIND_TIME_LAUNCHES, BIND_ROCTX, BIND_OVERLAP, HIP_LIB, HOSTONLY_LIB, SYMBOLS,
                    OK, E_ARG, E_INDEX, E_DOUBLE_READY, E_INCOMPLETE, E_STATE, E_HIP, E_NOMEM)
 from .reducer import Reducer, StepTable  # noqa: F401
 

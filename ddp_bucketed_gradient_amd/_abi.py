@@ -16,7 +16,7 @@ HOSTONLY_LIB = os.path.join(_HERE, "lib", "libddpb_hostonly.so")
 
 F32, BF16 = 0, 1
 MODE_FUSED, MODE_STAGED = 0, 1
-BIND_DEVICE_TIMESTAMPS, BIND_TIME_LAUNCHES, BIND_ROCTX = 1, 2, 4
+BIND_DEVICE_TIMESTAMPS, BIND_TIME_LAUNCHES, BIND_ROCTX, BIND_OVERLAP = 1, 2, 4, 8
 
 STATIC_SCRATCH_BYTES = 32 << 20      # DDPB_STATIC_SCRATCH_BYTES
 

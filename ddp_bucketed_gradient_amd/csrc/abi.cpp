@@ -137,7 +137,7 @@ int ddpb_bind(ddpb_t h, void* const* grad_ptrs, void* workspace, int64_t ws_byte
   if (!h) return fail(DDPB_E_ARG, "bind: NULL handle");
   const ddpb::Plan& p = h->red.plan();
   if (mode != DDPB_MODE_FUSED && mode != DDPB_MODE_STAGED) return fail(DDPB_E_ARG, "bind: bad mode");
-  if (flags & ~(DDPB_BIND_DEVICE_TIMESTAMPS | DDPB_BIND_TIME_LAUNCHES | DDPB_BIND_ROCTX)) return fail(DDPB_E_ARG, "bind: bad flags");
+  if (flags & ~(DDPB_BIND_DEVICE_TIMESTAMPS | DDPB_BIND_TIME_LAUNCHES | DDPB_BIND_ROCTX | DDPB_BIND_OVERLAP)) return fail(DDPB_E_ARG, "bind: bad flags");
   if (n_side < 1 || n_side > 16 || side_streams == nullptr) return fail(DDPB_E_ARG, "bind: need 1..16 side streams");
   const int64_t need = ddpb::workspace_bytes(p, mode);
   if (ws_bytes < need || (need > 0 && workspace == nullptr))
@@ -208,7 +208,7 @@ int ddpb_bind_bucket_views(ddpb_t h, void* const* replica_storage, int64_t stora
                            void* const* side_streams, int32_t n_side, int32_t flags) {
   if (!h) return fail(DDPB_E_ARG, "bind_bucket_views: NULL handle");
   const ddpb::Plan& p = h->red.plan();
-  if (flags & ~(DDPB_BIND_DEVICE_TIMESTAMPS | DDPB_BIND_TIME_LAUNCHES | DDPB_BIND_ROCTX))
+  if (flags & ~(DDPB_BIND_DEVICE_TIMESTAMPS | DDPB_BIND_TIME_LAUNCHES | DDPB_BIND_ROCTX | DDPB_BIND_OVERLAP))
     return fail(DDPB_E_ARG, "bind_bucket_views: bad flags");
   if (n_side < 1 || n_side > 16 || side_streams == nullptr)
     return fail(DDPB_E_ARG, "bind_bucket_views: need 1..16 side streams");

@@ -995,6 +995,9 @@ class HipLauncher final : public Launcher {
       for (auto& e : ev_t0_) HIP_OK(hipEventCreateWithFlags(&e, hipEventDisableSystemFence), "hipEventCreate");
       for (auto& e : ev_t1_) HIP_OK(hipEventCreateWithFlags(&e, hipEventDisableSystemFence), "hipEventCreate");
     }
+    // DDPB_BIND_OVERLAP: reduction workgroups may share CUs (with each other
+    // and with the backward's kernels).
+    if (flags_ & 8) wg_per_cu_ = 0;
     return update_lds_reserve(err);
   }
 

@@ -11,7 +11,8 @@ import sys as _sys
 from typing import List, Optional, Sequence
 
 from . import _abi
-from ._abi import BF16, F32, MODE_FUSED, MODE_STAGED, BIND_DEVICE_TIMESTAMPS, BIND_TIME_LAUNCHES, BIND_ROCTX  # noqa: F401
+from ._abi import (BF16, F32, MODE_FUSED, MODE_STAGED, BIND_DEVICE_TIMESTAMPS, BIND_TIME_LAUNCHES,  # noqa: F401
+                   BIND_ROCTX, BIND_OVERLAP)
 
 MiB = 1 << 20
 

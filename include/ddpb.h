@@ -61,9 +61,16 @@ enum {
                                       cost about 10 % of the throughput of a BERT-large sync */
   DDPB_BIND_TIME_LAUNCHES = 2,     /* hipEvents around each bucket's kernels (ddpb_get_launch_times);
                                       about 0.8 % of that throughput */
-  DDPB_BIND_ROCTX = 4              /* host-side roctx ranges around each launch of complete buckets
+  DDPB_BIND_ROCTX = 4,             /* host-side roctx ranges around each launch of complete buckets
                                       ("ddpb launch b0-b1"), the finalize join, no_sync_accumulate and
                                       set_sync_step, for rocprofv3 --marker-trace; no device work */
+  DDPB_BIND_OVERLAP = 8            /* the reductions will run beside a backward on the compute stream:
+                                      start with no per-CU limit on reduction workgroups (the
+                                      same setting as ddpb_set_workgroups_per_cu(h, 0), which
+                                      stays until changed) instead of one per CU, which
+                                      hid more of the reduction behind a bf16 MLP backward of many
+                                      buckets ([PDTI] §3.1, [Li] "Overlapping Computation with
+                                      Communication"); a standalone sync runs faster without it */
 };
 
 /* status codes */

@@ -387,15 +387,16 @@ def test_step_table_checks_before_the_library(host):
 
 
 def test_bind_flags(host):
-    """ddpb_bind takes DDPB_BIND_DEVICE_TIMESTAMPS, DDPB_BIND_TIME_LAUNCHES and
-    DDPB_BIND_ROCTX in any combination and refuses unknown bits."""
+    """ddpb_bind takes DDPB_BIND_DEVICE_TIMESTAMPS, DDPB_BIND_TIME_LAUNCHES,
+    DDPB_BIND_ROCTX and DDPB_BIND_OVERLAP in any combination and refuses
+    unknown bits."""
     red = _reducer(host, [10, 20], 2, 0)
     ptrs = [0x1000 + 16 * i for i in range(4)]
-    for f in (0, D.BIND_DEVICE_TIMESTAMPS, D.BIND_TIME_LAUNCHES, D.BIND_ROCTX,
-              D.BIND_DEVICE_TIMESTAMPS | D.BIND_TIME_LAUNCHES | D.BIND_ROCTX):
+    for f in (0, D.BIND_DEVICE_TIMESTAMPS, D.BIND_TIME_LAUNCHES, D.BIND_ROCTX, D.BIND_OVERLAP,
+              D.BIND_DEVICE_TIMESTAMPS | D.BIND_TIME_LAUNCHES | D.BIND_ROCTX | D.BIND_OVERLAP):
         red.bind_ptrs(ptrs, side_streams=[0], flags=f)
         red.sync()
-    for bad in (8, 1 << 20, -1):
+    for bad in (16, 1 << 20, -1):
         with pytest.raises(D.DdpbError) as e:
             red.bind_ptrs(ptrs, side_streams=[0], flags=bad)
         assert e.value.code == D.E_ARG

@@ -1,0 +1,109 @@
+"""CPU tests of the profiling summaries (ddp_bucketed_gradient_amd.profiling)
+on small synthetic rocprofv3 CSV files: interval unions and intersections by
+brute force, the per-sync grouping of a kernel trace, marker-delimited overlap
+and the copy-calibrated counter traffic."""
+import csv
+import json
+
+import numpy as np
+import pytest
+
+from ddp_bucketed_gradient_amd import profiling as PF
+
+
+def _brute_union(iv, res=1):
+    """Length of a union of integer intervals by marking unit cells."""
+    if not iv:
+        return 0
+    lo, hi = min(s for s, _ in iv), max(e for _, e in iv)
+    cells = np.zeros(hi - lo, bool)
+    for s, e in iv:
+        cells[s - lo:e - lo] = True
+    return int(cells.sum())
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_union_and_intersection_against_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    iv = [(int(s), int(s + d)) for s, d in zip(rng.integers(0, 200, 12), rng.integers(0, 40, 12))]
+    assert PF.union_length([s for s, _ in iv], [e - s for s, e in iv]) == _brute_union(iv)
+    other = [(int(s), int(s + d)) for s, d in zip(rng.integers(0, 200, 9), rng.integers(1, 30, 9))]
+    m = PF.merge(other)
+    for a in iv:
+        both = _brute_union([a]) + _brute_union(other) - _brute_union([a] + other)
+        assert PF.intersection_length(a, m) == both
+
+
+def _write_trace(path, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kind", "Agent_Id", "Queue_Id", "Stream_Id", "Thread_Id", "Dispatch_Id", "Kernel_Id",
+                    "Kernel_Name", "Correlation_Id", "Start_Timestamp", "End_Timestamp"])
+        for i, (name, s, e) in enumerate(rows):
+            w.writerow(["KERNEL_DISPATCH", "Agent 1", 1, 1, 1, i + 1, 7, name, i + 1, s, e])
+
+
+def test_trace_summary_groups_syncs_and_takes_unions(tmp_path):
+    # two warm-up syncs, then two timed syncs of three launches, two streams overlapping
+    rows = [("gen", 0, 50)]
+    t = 100
+    for sync in range(4):
+        rows += [("void ddpb::fused_mean_kernel<8, true>(x)", t, t + 100),
+                 ("void ddpb::fused_mean_kernel<8, true>(x)", t + 50, t + 150),
+                 ("copyBuffer", t + 160, t + 170),
+                 ("void ddpb::fused_mean_kernel<8, true>(x)", t + 150, t + 200)]
+        t += 1000
+    _write_trace(tmp_path / "run_kernel_trace.csv", rows)
+    d = PF.read_dispatches(str(tmp_path))
+    out = PF.trace_summary(d, "fused_mean_kernel", per_sync=3, timed=2, alg_bytes=800.0, peak=8.0)
+    assert out["busy_us_per_sync"] == 0.2                     # union 200 ns of 250 ns of launches
+    assert out["avg_launch_us"] == round(250 / 3 / 1e3, 2)
+    assert out["GBps_union"] == 4.0 and out["frac_union"] == 0.5
+    assert out["launch_concurrency"] == 1.25
+    assert out["span_us_per_sync"] == round((1000 + 200) / 2 / 1e3, 2)
+    with pytest.raises(ValueError):
+        PF.trace_summary(d, "fused_mean_kernel", per_sync=3, timed=5, alg_bytes=1.0)
+
+
+def test_overlap_summary_counts_only_the_phase_windows(tmp_path):
+    rows = [("fused_mean_kernel<8,true>", 0, 100),             # outside every window
+            ("Cijk_gemm", 1000, 1100),
+            ("fused_mean_kernel<8,true>", 1050, 1150),         # 50 with the GEMM
+            ("reduce_kernel", 1140, 1200),                     # +10 with another kernel
+            ("fused_mean_kernel<8,true>", 1300, 1400)]         # alone
+    _write_trace(tmp_path / "run_kernel_trace.csv", rows)
+    with open(tmp_path / "run_marker_api_trace.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Domain", "Function", "Start_Timestamp", "End_Timestamp"])
+        w.writerow(["MARKER_CORE_API", "bench both wg0 blocks0", 900, 2000])
+        w.writerow(["MARKER_CORE_API", "bench reduction alone wg0 blocks0", 0, 500])
+    out = PF.overlap_summary(PF.read_dispatches(str(tmp_path)), PF.read_markers(str(tmp_path)),
+                             "fused_mean_kernel", "^bench both", "Cijk")
+    assert out["reduction_launches"] == 2
+    assert out["frac_concurrent_with_compute"] == 0.25
+    assert out["frac_concurrent_with_any_kernel"] == 0.3
+
+
+def test_traffic_summary_calibrates_on_copies(tmp_path):
+    def counters(path, name, copy_kib, vals):
+        with open(path, "w", newline="") as f:
+            w = csv.writer(f)
+            w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+            k = 0
+            for v in copy_kib:
+                k += 1
+                w.writerow([k, "__amd_rocclr_copyBuffer", name, v])
+            for v in vals:
+                k += 1
+                w.writerow([k, "accumulate_kernel<true, false>", name, v])
+    counters(tmp_path / "f_counter_collection.csv", "FETCH_SIZE", [1000.0, 1000.0, 3.0], [10.0, 30.0])
+    counters(tmp_path / "w_counter_collection.csv", "WRITE_SIZE", [2000.0, 2000.0], [10.0, 10.0])
+    out = PF.traffic_summary(PF.read_counter(str(tmp_path / "f_counter_collection.csv"), "FETCH_SIZE"),
+                             PF.read_counter(str(tmp_path / "w_counter_collection.csv"), "WRITE_SIZE"),
+                             "accumulate_kernel", copy_bytes=2048000.0, alg_bytes_per_launch=51200.0)
+    assert out["fetch_scale"] == 2.0 and out["write_scale"] == 1.0
+    assert out["fetch_bytes_per_launch"] == 20 * 1024 * 2 and out["write_bytes_per_launch"] == 10 * 1024
+    assert out["traffic_over_algorithmic"] == 1.0
+    p = tmp_path / "traffic.json"
+    PF.update_traffic_json(str(p), "k:w", out)
+    assert json.loads(p.read_text())["k:w"]["bytes_per_launch"] == 51200
