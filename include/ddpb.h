@@ -158,15 +158,18 @@ int ddpb_bind(ddpb_t h, void* const* grad_ptrs, void* workspace, int64_t ws_byte
               void* compute_stream, void* const* side_streams, int32_t n_side,
               int32_t mode, int32_t flags);
 
-/* Binding for callers that cannot allocate device memory: code being
- * captured into a HIP graph, tight serving loops, harnesses that forbid
- * hipMalloc. Same as ddpb_bind (grad_ptrs, compute_stream and mode mean the
+/* Binding for callers that cannot allocate device memory: tight serving
+ * loops, harnesses that forbid hipMalloc, programs that capture their steps
+ * into HIP graphs and keep allocation out of them. Same as ddpb_bind (grad_ptrs, compute_stream and mode mean the
  * same) except that the library allocates nothing: its pointer and segment
  * tables and, in DDPB_MODE_STAGED, its flat buckets (no workspace argument)
  * are placed in a static device array of DDPB_STATIC_SCRATCH_BYTES bytes
  * that every device the library runs on holds until the process ends. No
  * hipMalloc, hipHostMalloc or hipEventCreate is called; the bucket reductions
  * run on the compute stream itself (no side streams, no events, no flags).
+ * The bind uploads the tables and synchronises the compute stream once, so it
+ * is not made during a capture; syncs on the binding may be captured and
+ * replayed as with ddpb_bind.
  * Needs round256(R*P*8) + round256(segments*32) bytes (ddpb_num_segments),
  * plus ddpb_workspace_bytes(STAGED) in staged mode; a larger model gets
  * DDPB_E_ARG and is left unbound.

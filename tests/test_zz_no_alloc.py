@@ -98,3 +98,41 @@ def test_static_binding_refuses_a_model_beyond_the_array():
     for r in range(R):
         assert_bits_equal(got[0][r], want, f"r={r}")
     red.close()
+
+
+def test_static_binding_sync_captured_and_replayed():
+    """A sync on a static binding recorded into a HIP graph and replayed three
+    times with eager work between the replays: every replay leaves the
+    oracle's bits (the inputs are refilled before each replay)."""
+    numels, R, cap = SMALL[0] + [9000], 4, 4 * 3000
+    red = D.Reducer([(n,) for n in numels], R, cap)
+    grads = alloc_grads(numels, R)
+    compute = torch.cuda.Stream()
+    with torch.cuda.stream(compute):
+        red.bind_static(grads, compute_stream=compute)
+        host, order, want, _ = _case(numels, R, cap, 60)
+        fill_from_host(grads, host)
+        red.sync(order)                        # eager sync first: same bits
+    got = snapshot(grads)
+    for v in range(len(numels)):
+        for r in range(R):
+            assert_bits_equal(got[v][r], want[r][v], f"eager v={v} r={r}")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=compute):
+        red.sync(order)
+    for rep in range(3):
+        host, _, _, _ = _case(numels, R, cap, 61 + rep)
+        orc = OR.Reducer(numels, R, cap)
+        og = [[h.copy() for h in row] for row in host]
+        orc.bind(og)
+        orc.sync(order)
+        with torch.cuda.stream(compute):
+            fill_from_host(grads, host)
+            torch.cuda.synchronize()
+            g.replay()
+        torch.cuda.synchronize()
+        got = snapshot(grads)
+        for v in range(len(numels)):
+            for r in range(R):
+                assert_bits_equal(got[v][r], og[r][v], f"replay {rep} v={v} r={r}")
+    red.close()
