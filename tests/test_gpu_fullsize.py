@@ -153,6 +153,88 @@ def test_config3_bert_large_every_element(cap_mib, bert_large_means, bert_large_
     red.close()
 
 
+def test_config3_staged_every_element(bert_large_means, bert_large_grads):
+    """The staged path (pack into flat buckets, mean, copy back) at full size,
+    as the bench's --mode staged binds it (12 GB of caller workspace)."""
+    w = WC.BERT_LARGE
+    numels = w.numels()
+    P, R = len(numels), w.R
+    say(f"{w.name} staged every element")
+    compute, sides = _bench_streams()
+    grads = bert_large_grads
+    red = D.Reducer([p.shape for p in w.params()], R, w.cap_bytes)
+    with torch.cuda.stream(compute):
+        red.bind(grads, compute_stream=compute, side_streams=sides, mode=D.MODE_STAGED,
+                 flags=D.BIND_TIME_LAUNCHES)
+        _fill(3, grads)
+        red.sync(w.ready_order())
+    torch.cuda.synchronize()
+    assert red.launch_log() == closed_form_launch_log(red.buckets(), w.ready_order())
+    for v in range(P):
+        want = to_device_f32(bert_large_means[v])
+        for r in range(R):
+            assert_device_bits_equal(grads[r][v], want, f"staged v={v} r={r}")
+    red.close()
+
+
+@pytest.mark.parametrize("R", [20, 32])
+def test_generic_replica_count_bert_large_every_element(R):
+    """BERT-large shapes at R = 20 and 32 (the bench's --replicas), where the
+    replica count is a run-time argument of the reduction kernel: every
+    element of every replica against the oracle's fixed-order mean."""
+    w = WC.BERT_LARGE
+    numels = w.numels()
+    P = len(numels)
+    say(f"{w.name} at R={R} every element")
+    compute, sides = _bench_streams()
+    grads = alloc_grads(numels, R)
+    red = D.Reducer([p.shape for p in w.params()], R, w.cap_bytes)
+    with torch.cuda.stream(compute):
+        red.bind(grads, compute_stream=compute, side_streams=sides, flags=D.BIND_TIME_LAUNCHES)
+        _fill(3, grads)
+        red.sync(w.ready_order())
+    torch.cuda.synchronize()
+    assert red.launch_log() == closed_form_launch_log(red.buckets(), w.ready_order())
+    stage = HostStage(R, max(numels))
+    out = np.empty(max(numels), np.float32)
+    with ThreadPoolExecutor(host_workers()) as pool:
+        for v, n in enumerate(numels):
+            _progress(v, P, f"oracle at R={R}")
+            bufs = [stage.fetch(r, _regen_dev(3, r, v, n)) for r in range(R)]
+            want = to_device_f32(_oracle_mean(pool, bufs, out[:n]))
+            for r in range(R):
+                assert_device_bits_equal(grads[r][v], want, f"R={R} v={v} r={r}")
+    red.close()
+    del grads
+
+
+@pytest.mark.parametrize("param_mib,cap_mib", [(4, 4), (4, 16), (4, 64), (1, 4), (1, 16), (1, 64)])
+def test_blog_payload_every_element(param_mib, cap_mib):
+    """The blog's 48 MiB payload per replica, R = 4, as 12 x 4 MiB or 48 x 1 MiB
+    parameters under caps of 4, 16 and 64 MiB (the bench's --config 6)."""
+    base = WC.BLOG_COARSE4 if param_mib == 4 else WC.BLOG_FINE1
+    numels = base.numels()
+    P, R, cap = len(numels), base.R, cap_mib * WS.MiB
+    say(f"{base.name} cap {cap_mib} MiB every element")
+    compute, sides = _bench_streams()
+    grads = alloc_grads(numels, R)
+    red = D.Reducer([p.shape for p in base.params()], R, cap)
+    with torch.cuda.stream(compute):
+        red.bind(grads, compute_stream=compute, side_streams=sides, flags=D.BIND_TIME_LAUNCHES)
+        _fill(base.cfg, grads)
+        red.sync(base.ready_order())
+    torch.cuda.synchronize()
+    assert red.buckets() == OP.compute_bucket_assignment_by_size(numels, 4, cap)
+    assert red.launch_log() == closed_form_launch_log(red.buckets(), base.ready_order())
+    with ThreadPoolExecutor(host_workers()) as pool:
+        for v, n in enumerate(numels):
+            bufs = [_regen_dev(base.cfg, r, v, n).cpu().numpy() for r in range(R)]
+            want = to_device_f32(_oracle_mean(pool, bufs, np.empty(n, np.float32)))
+            for r in range(R):
+                assert_device_bits_equal(grads[r][v], want, f"blog v={v} r={r}")
+    red.close()
+
+
 def test_bucket_view_bert_large_every_element(bert_large_means, bert_large_grads):
     """gradient_as_bucket_view at full size: the gradients are views of one flat
     storage per replica, as the bench's --mode view binds them."""
