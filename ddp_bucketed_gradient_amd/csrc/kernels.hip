@@ -905,8 +905,9 @@ class HipLauncher final : public Launcher {
   ~HipLauncher() override { release(); }
 
   int bind(const Plan& plan, const BindArgs& a, std::string* err) override {
+    const bool held_static = static_;
     release();
-    if (a.no_alloc) return bind_static(plan, a, err);
+    if (a.no_alloc) return bind_static(plan, a, held_static, err);
     plan_ = &plan;
     R_ = plan.R;
     P_ = plan.P;
@@ -1224,7 +1225,7 @@ class HipLauncher final : public Launcher {
   // mode's flat buckets) are placed in this device's copy of `scratch`; the
   // reductions run on the compute stream, so no event is needed either.
   // Calls no hipMalloc, hipHostMalloc or hipEventCreate.
-  int bind_static(const Plan& plan, const BindArgs& a, std::string* err) {
+  int bind_static(const Plan& plan, const BindArgs& a, bool held_static, std::string* err) {
     plan_ = &plan;
     R_ = plan.R;
     P_ = plan.P;
@@ -1260,9 +1261,11 @@ class HipLauncher final : public Launcher {
       g_scratch_owner[device_] = this;
     }
     static_ = true;
-    // The previous holder's reductions may still read the tables: let the
-    // device drain before they are overwritten.
-    if (prev != nullptr && prev != this) HIP_OK(hipDeviceSynchronize(), "bind_static: synchronize");
+    // The previous holder's reductions (another handle's, or this handle's
+    // own earlier static binding, perhaps on another stream) may still read
+    // the tables: let the device drain before they are overwritten.
+    if ((prev != nullptr && prev != this) || held_static)
+      HIP_OK(hipDeviceSynchronize(), "bind_static: synchronize");
     d_grads_ = reinterpret_cast<float**>(base);
     d_segs_ = reinterpret_cast<Segment*>(base + off_segs);
     if (mode_ == kModeStaged) {

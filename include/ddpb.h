@@ -174,8 +174,8 @@ int ddpb_bind(ddpb_t h, void* const* grad_ptrs, void* workspace, int64_t ws_byte
  * plus ddpb_workspace_bytes(STAGED) in staged mode; a larger model gets
  * DDPB_E_ARG and is left unbound.
  * The array is shared by every static binding on a device and keeps the last
- * binding's tables: a later ddpb_bind_static on the same device waits for the
- * device to drain and takes the array over, after which the earlier handle's
+ * binding's tables: a later ddpb_bind_static on the same device (by this
+ * handle or another) waits for the device to drain and takes the array over, after which the earlier handle's
  * launches fail with DDPB_E_STATE until it is bound again. Static bindings of
  * one device used from several threads at once race. Nothing in the array
  * needs to start at zero (every byte the kernels read is written first).

@@ -136,3 +136,35 @@ def test_static_binding_sync_captured_and_replayed():
             for r in range(R):
                 assert_bits_equal(got[v][r], og[r][v], f"replay {rep} v={v} r={r}")
     red.close()
+
+
+def test_static_rebind_of_the_same_handle_on_another_stream():
+    """A static binding re-bound by the same handle onto another compute stream
+    while its last sync may still run: the rebind drains the device before it
+    rewrites the array, so both syncs leave the oracle's bits."""
+    numels, R, cap = BIG[0], 8, BIG[2]
+    red = D.Reducer([(n,) for n in numels], R, cap)
+    ga, gb = alloc_grads(numels, R), alloc_grads(numels, R)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    host_a, order, want_a, _ = _case(numels, R, cap, 70)
+    host_b, _, _, _ = _case(numels, R, cap, 71)
+    fill_from_host(ga, host_a)
+    fill_from_host(gb, host_b)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(sa):
+        red.bind_static(ga, compute_stream=sa)
+        red.sync(order)                        # not waited for before the rebind
+    with torch.cuda.stream(sb):
+        red.bind_static(gb, compute_stream=sb)
+        red.sync(order)
+    torch.cuda.synchronize()
+    orc = OR.Reducer(numels, R, cap)
+    og = [[h.copy() for h in row] for row in host_b]
+    orc.bind(og)
+    orc.sync(order)
+    got_a, got_b = snapshot(ga), snapshot(gb)
+    for v in range(len(numels)):
+        for r in range(R):
+            assert_bits_equal(got_a[v][r], want_a[r][v], f"first binding v={v} r={r}")
+            assert_bits_equal(got_b[v][r], og[r][v], f"second binding v={v} r={r}")
+    red.close()
