@@ -109,20 +109,20 @@ def parse():
     return ap.parse_args()
 
 
-from ddp_bucketed_gradient_amd.profiling import kernel_source_hash, union_length  # noqa: E402
+from ddp_bucketed_gradient_amd.profiling import stored_figure_current, union_length  # noqa: E402
 
 
 def overlap_from_profiles(workload: str, setting: str):
     """The timeline figure of a --config 5 phase (share of the reduction
     kernels' time concurrent with backward kernels) from the kernel and
-    marker trace summarised under profiles/; only while the kernel sources
-    are unchanged."""
+    marker trace summarised under profiles/; only while the built kernels are
+    the ones measured."""
     p = os.path.join(ROOT, "profiles", "overlap.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
         e = json.load(f).get(workload)
-    if not e or e.get("kernel_source_sha256_16") != kernel_source_hash():
+    if not e or not stored_figure_current(e):
         return None
     ph = e["phases"].get(setting)
     return dict(ph, profile=e["profile"]) if ph else None
@@ -130,14 +130,15 @@ def overlap_from_profiles(workload: str, setting: str):
 
 def traffic_from_profiles(kernel: str, workload: str):
     """HBM bytes per launch measured with rocprofv3 FETCH_SIZE/WRITE_SIZE and
-    stored under profiles/; only used while the kernel source is unchanged."""
+    stored under profiles/; only used while the built kernels are the ones
+    measured (the device code's hash)."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
         d = json.load(f)
     e = d.get(f"{kernel}:{workload}")
-    if not e or e.get("kernel_source_sha256_16") != kernel_source_hash():
+    if not e or not stored_figure_current(e):
         return None
     return e.get("bytes_per_launch")
 

@@ -47,6 +47,38 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def device_code_hash(lib_path: Optional[str] = None) -> Optional[str]:
+    """sha256 prefix of the gfx950 device code in the built library (its
+    `.hip_fatbin` section): it changes exactly when a kernel's compiled code
+    changes, not when only host code does. None if the library is missing."""
+    import struct
+    path = lib_path or os.path.join(ROOT, "ddp_bucketed_gradient_amd", "lib", "libddpb.so")
+    if not os.path.exists(path):
+        return None
+    with open(path, "rb") as f:
+        d = f.read()
+    if d[:4] != b"\x7fELF" or d[4] != 2:
+        return None
+    shoff = struct.unpack_from("<Q", d, 0x28)[0]
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", d, 0x3A)
+    secs = [struct.unpack_from("<IIQQQQIIQQ", d, shoff + i * shentsize) for i in range(shnum)]
+    stroff = secs[shstrndx][4]
+    for sec in secs:
+        name = d[stroff + sec[0]:d.index(b"\0", stroff + sec[0])]
+        if name == b".hip_fatbin":
+            return hashlib.sha256(d[sec[4]:sec[4] + sec[5]]).hexdigest()[:16]
+    return None
+
+
+def stored_figure_current(entry: dict) -> bool:
+    """Whether a figure stored under profiles/ was measured with the kernels
+    now built: by the device-code hash when the entry has one, else by the
+    kernel-source hash."""
+    if entry.get("device_code_sha256_16"):
+        return entry["device_code_sha256_16"] == device_code_hash()
+    return entry.get("kernel_source_sha256_16") == kernel_source_hash()
+
+
 def union_length(starts: Sequence[float], durs: Sequence[float]) -> float:
     """Length of the union of the intervals [s, s + d)."""
     return sum(e - s for s, e in merge([(s, s + d) for s, d in zip(starts, durs)]))
@@ -204,6 +236,7 @@ def traffic_summary(fetch: List[Tuple[str, float]], write: List[Tuple[str, float
     w_kib, nlw = per_launch(write)
     fb, wb = f_kib * 1024 * sf, w_kib * 1024 * sw
     return {"kernel": kernel, "kernel_source_sha256_16": kernel_source_hash(),
+            "device_code_sha256_16": device_code_hash(),
             "fetch_bytes_per_launch": round(fb), "write_bytes_per_launch": round(wb),
             "bytes_per_launch": round(fb + wb), "alg_bytes_per_launch": round(alg_bytes_per_launch),
             "traffic_over_algorithmic": round((fb + wb) / alg_bytes_per_launch, 4),

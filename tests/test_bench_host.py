@@ -38,23 +38,37 @@ def test_union_length_matches_brute_force():
         assert bench.union_length(st, du) == pytest.approx(len(covered))
 
 
-def test_traffic_only_for_the_measured_sources(tmp_path, monkeypatch):
+def test_traffic_only_for_the_measured_kernels(tmp_path, monkeypatch):
+    """A stored counter figure is reported only while the built device code is
+    the one measured (its hash), or, for an entry without one, while the
+    kernel sources are."""
+    from ddp_bucketed_gradient_amd import profiling as PF
     key = "fused_mean_kernel:some_workload"
     prof = tmp_path / "profiles"
     prof.mkdir()
-    entry = {"kernel_source_sha256_16": bench.kernel_source_hash(), "bytes_per_launch": 1234}
-    (prof / "traffic.json").write_text(json.dumps({key: entry}))
+    entry = {"device_code_sha256_16": "ab" * 8, "bytes_per_launch": 1234}
+    old = {"kernel_source_sha256_16": "cd" * 8, "bytes_per_launch": 99}
+    (prof / "traffic.json").write_text(json.dumps({key: entry, "k:old": old}))
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    monkeypatch.setattr(bench, "kernel_source_hash", lambda: entry["kernel_source_sha256_16"])
+    monkeypatch.setattr(PF, "device_code_hash", lambda lib_path=None: "ab" * 8)
+    monkeypatch.setattr(PF, "kernel_source_hash", lambda: "cd" * 8)
     assert bench.traffic_from_profiles("fused_mean_kernel", "some_workload") == 1234
     assert bench.traffic_from_profiles("fused_mean_kernel", "other_workload") is None
-    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)    # sources changed since
+    assert bench.traffic_from_profiles("k", "old") == 99
+    monkeypatch.setattr(PF, "device_code_hash", lambda lib_path=None: "0" * 16)    # kernels rebuilt since
+    monkeypatch.setattr(PF, "kernel_source_hash", lambda: "0" * 16)
     assert bench.traffic_from_profiles("fused_mean_kernel", "some_workload") is None
+    assert bench.traffic_from_profiles("k", "old") is None
 
 
-def test_kernel_source_hash_covers_the_kernel_sources():
-    h = bench.kernel_source_hash()
+def test_hashes_of_the_kernels():
+    from ddp_bucketed_gradient_amd import profiling as PF
+    h = PF.kernel_source_hash()
     assert len(h) == 16 and int(h, 16) >= 0
+    d = PF.device_code_hash()
+    if d is not None:                      # the built library's gfx950 code
+        assert len(d) == 16 and d == PF.device_code_hash()
+    assert PF.device_code_hash("/nonexistent/lib.so") is None
 
 
 def test_more_than_one_gpu_is_refused():
