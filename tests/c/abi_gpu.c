@@ -6,7 +6,8 @@
  *   abi_gpu <input file> <output file>
  *
  * Input (little-endian): int32 magic 0x44445042, int32 P, int32 R, int32 mode
- * (DDPB_MODE_FUSED or DDPB_MODE_STAGED), int64 cap, int64 numel[P], int32 n,
+ * (DDPB_MODE_FUSED or DDPB_MODE_STAGED, plus 2 to bind with ddpb_bind_static,
+ * which allocates nothing and reduces on the compute stream), int64 cap, int64 numel[P], int32 n,
  * int32 order[n] (the hooks, in firing order), then float32 gradients of
  * replica 0 variable 0, replica 0 variable 1, ... replica R-1 variable P-1.
  * Output: the gradients after ddpb_finalize in the same layout, then int32 m
@@ -49,10 +50,12 @@ int main(int argc, char** argv) {
   int64_t cap = 0;
   if (!read_all(in, &magic, 4) || magic != 0x44445042 || !read_all(in, &P, 4) || !read_all(in, &R, 4) ||
       !read_all(in, &mode, 4) || !read_all(in, &cap, 8) || P < 1 || P > 4096 || R < 1 || R > 64 ||
-      (mode != DDPB_MODE_FUSED && mode != DDPB_MODE_STAGED)) {
+      mode < 0 || mode > 3) {
     fprintf(stderr, "bad header\n");
     return 1;
   }
+  const int use_static = (mode & 2) != 0;
+  mode &= 1;
   int64_t* numel = malloc(sizeof(int64_t) * (size_t)P);
   int32_t* ndims = malloc(sizeof(int32_t) * (size_t)P);
   if (!numel || !ndims || !read_all(in, numel, sizeof(int64_t) * (size_t)P) || !read_all(in, &n, 4) || n < 0 ||
@@ -97,10 +100,14 @@ int main(int argc, char** argv) {
   HIPCHECK(hipStreamCreate(&side[1]));
   int64_t ws_bytes = 0;
   void* ws = NULL;
-  DDPBCHECK(ddpb_workspace_bytes(h, mode, &ws_bytes));
-  if (ws_bytes > 0) HIPCHECK(hipMalloc(&ws, (size_t)ws_bytes));
-  void* sides[2] = {side[0], side[1]};
-  DDPBCHECK(ddpb_bind(h, grads, ws, ws_bytes, compute, sides, 2, mode, 0));
+  if (use_static) {
+    DDPBCHECK(ddpb_bind_static(h, grads, compute, mode));  /* no workspace, nothing allocated */
+  } else {
+    DDPBCHECK(ddpb_workspace_bytes(h, mode, &ws_bytes));
+    if (ws_bytes > 0) HIPCHECK(hipMalloc(&ws, (size_t)ws_bytes));
+    void* sides[2] = {side[0], side[1]};
+    DDPBCHECK(ddpb_bind(h, grads, ws, ws_bytes, compute, sides, 2, mode, 0));
+  }
   for (int32_t i = 0; i < n; ++i) DDPBCHECK(ddpb_mark_ready(h, order[i]));
   DDPBCHECK(ddpb_finalize(h));
   HIPCHECK(hipStreamSynchronize(compute));

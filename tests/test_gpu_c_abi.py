@@ -3,7 +3,7 @@ Python or torch in the data path. This test writes seeded inputs and the hook
 order to a file, the C program allocates the replicas' gradients with
 hipMalloc, binds them, fires the hooks, finalizes and writes the gradients
 back out; the result must equal the oracle's bit for bit, and so must the
-launch log."""
+launch log. The same program also binds with ddpb_bind_static."""
 import os
 import shutil
 import struct
@@ -44,6 +44,10 @@ CASES = [
     ([5, 300, 4100, 3, 8193, 64], 3, 4 * 5000, D.MODE_FUSED),
     ([5, 300, 4100, 3, 8193, 64], 8, 4 * 5000, D.MODE_STAGED),
     ([1000, 0, 20000, 7], 20, 0, D.MODE_FUSED),
+    # + 2: bound with ddpb_bind_static (no allocation, reductions on the compute stream)
+    ([5, 300, 4100, 3, 8193, 64], 3, 4 * 5000, D.MODE_FUSED + 2),
+    ([5, 300, 4100, 3, 8193, 64], 8, 4 * 5000, D.MODE_STAGED + 2),
+    ([1000, 0, 20000, 7], 20, 0, D.MODE_FUSED + 2),
 ]
 
 
