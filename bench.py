@@ -590,6 +590,7 @@ def nosync_oracle_unit(numels_s, R, k, cap, host_steps):
             orc.no_sync_accumulate(host_steps[t], first=(t == 0))
         orc.sync()
         return nbytes
+    unit.reducer = orc               # (its gradients, for checking the unit)
     return unit
 
 

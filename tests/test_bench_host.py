@@ -112,3 +112,64 @@ def test_replicas_out_of_range_is_refused():
     for bad in ("0", "65"):
         with pytest.raises(SystemExit):
             bench.sync_workload(_args(["--replicas", bad]), WC)
+
+
+def test_nosync_oracle_unit_matches_the_oracle_path():
+    """The config-4 CPU baseline's unit (k micro-steps accumulated, then the
+    bucketed sync, in one oracle reducer reused across units) leaves the same
+    bits as a fresh oracle run, every time it runs, and counts the line's
+    algorithmic bytes."""
+    import numpy as np
+    from oracle import reducer as OR
+    from workloads import gen as WG
+    numels, R, k, cap = [300, 7, 1000], 4, 3, 4 * 600
+    N = sum(numels)
+    steps = [[[WG.normal(WG.seed_of(4, r, v, t), n).to(__import__("torch").bfloat16)
+               .view(__import__("torch").int16).numpy().view(np.uint16) for v, n in enumerate(numels)]
+              for r in range(R)] for t in range(k)]
+    unit = bench.nosync_oracle_unit(numels, R, k, cap, steps)
+    for _ in range(2):
+        assert unit() == R * N * (6 + 10 * (k - 1)) + 2 * R * 4 * N
+    ref = OR.Reducer(numels, R, cap)
+    acc = [[np.zeros(n, np.float32) for n in numels] for _ in range(R)]
+    ref.bind(acc)
+    ref.set_sync(False)
+    for t in range(k):
+        if t == k - 1:
+            ref.set_sync(True)
+        ref.no_sync_accumulate(steps[t], first=(t == 0))
+    ref.sync()
+    got = unit.reducer.grads                  # the unit's own accumulators
+    for r in range(R):
+        for v in range(len(numels)):
+            assert np.array_equal(got[r][v].view(np.uint32), acc[r][v].view(np.uint32))
+
+
+def test_time_oracle_threads_counts_bytes_over_time():
+    calls = []
+
+    def make(g):
+        def unit():
+            calls.append(g)
+            return 1000
+        return unit
+    gbs, dt, reps = bench.time_oracle_threads(make, [0, 1, 2], 0.05)
+    assert dt >= 0.05 and reps >= 1
+    assert gbs == pytest.approx(1000 * (len(calls) - 3) / dt / 1e9, rel=0.05)
+
+
+def test_ceiling_plan_holds_the_syncs_bytes():
+    """The ceiling leg numbers each replica's copy of each variable as its own
+    variable (variable-major) at R = 1 under R times the cap: the same bytes in
+    about the same number of buckets as the R-replica plan."""
+    from oracle import plan as OP
+    from workloads import configs as WC
+    for w in (WC.BERT_LARGE, WC.RESNET50):
+        numels, R = w.numels(), w.R
+        vm = [numels[v] for v in range(len(numels)) for _ in range(R)]
+        b_sync = OP.compute_bucket_assignment_by_size(numels, 4, w.cap_bytes)
+        b_ceil = OP.compute_bucket_assignment_by_size(vm, 4, R * w.cap_bytes)
+        assert sum(OP.bucket_numels(b_ceil, vm)) == R * sum(numels)
+        assert abs(len(b_ceil) - len(b_sync)) <= len(b_sync) // 2
+        # reverse order visits the R copies of each variable together
+        assert b_ceil[0][:R] == list(range(len(vm) - 1, len(vm) - 1 - R, -1))
