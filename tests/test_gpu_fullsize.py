@@ -235,6 +235,36 @@ def test_blog_payload_every_element(param_mib, cap_mib):
     red.close()
 
 
+def test_graph_replay_bert_large_every_element(bert_large_means, bert_large_grads):
+    """A whole BERT-large sync captured into a HIP graph on the compute stream
+    and replayed (the bench's --graph), twice, the inputs drawn again before
+    each replay: every element of every replica against the oracle."""
+    w = WC.BERT_LARGE
+    numels = w.numels()
+    P, R = len(numels), w.R
+    say(f"{w.name} graph replay every element")
+    compute, sides = _bench_streams()
+    grads = bert_large_grads
+    red = D.Reducer([p.shape for p in w.params()], R, w.cap_bytes)
+    with torch.cuda.stream(compute):
+        red.bind(grads, compute_stream=compute, side_streams=sides)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=compute):
+        red.sync(w.ready_order())
+    torch.cuda.synchronize()
+    for rep in range(2):
+        with torch.cuda.stream(compute):
+            _fill(3, grads)
+            g.replay()
+        torch.cuda.synchronize()
+        for v in range(P):
+            want = to_device_f32(bert_large_means[v])
+            for r in range(R):
+                assert_device_bits_equal(grads[r][v], want, f"replay {rep} v={v} r={r}")
+    red.close()
+
+
 def test_bucket_view_bert_large_every_element(bert_large_means, bert_large_grads):
     """gradient_as_bucket_view at full size: the gradients are views of one flat
     storage per replica, as the bench's --mode view binds them."""
