@@ -91,6 +91,19 @@ int main(void) {
   CHECK(n == 3 && lb[0] == 0 && lb[1] == 1 && lb[2] == 2);
   CHECK(trig[0] == 2 && trig[1] == 2 && trig[2] == 2);
   CHECK(ddpb_finalize(h) == DDPB_OK);
+
+  /* the allocation-free binding: argument checks, then a sync; the calls that
+     need pinned staging are refused on it */
+  void* null_grads[6] = {0};
+  CHECK(ddpb_bind_static(h, grads, NULL, 5) == DDPB_E_ARG);            /* bad mode */
+  CHECK(ddpb_bind_static(h, null_grads, NULL, DDPB_MODE_FUSED) == DDPB_E_ARG);
+  CHECK(ddpb_bind_static(NULL, grads, NULL, DDPB_MODE_FUSED) == DDPB_E_ARG);
+  CHECK(ddpb_bind_static(h, grads, NULL, DDPB_MODE_STAGED) == DDPB_OK);
+  CHECK(ddpb_no_sync_accumulate(h, grads, DDPB_F32, 1) == DDPB_E_STATE);
+  uint8_t used[6] = {1, 1, 1, 1, 1, 1};
+  CHECK(ddpb_set_local_used(h, used) == DDPB_E_STATE);
+  CHECK(ddpb_mark_ready(h, 2) == DDPB_OK && ddpb_mark_ready(h, 1) == DDPB_OK && ddpb_mark_ready(h, 0) == DDPB_OK);
+  CHECK(ddpb_finalize(h) == DDPB_OK);
   ddpb_destroy(h);
 
   if (failures) {
