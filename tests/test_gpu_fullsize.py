@@ -517,3 +517,72 @@ def test_config5_overlap_every_element(size, wg):
             for r in range(R):
                 assert_device_bits_equal(grads[r][v], want, f"config5 {size} v={v} r={r}")
     red.close()
+
+
+def test_config5_rebuilt_from_shuffled_order_every_element():
+    """The bench's --config 5 --shuffle-params --rebuild at full size: the 96
+    parameters are defined in a seeded shuffled order, a first iteration runs
+    as one bucket and records the hook order, the buckets are rebuilt from it
+    (same cap) and bound again, and the second iteration's overlapped backward
+    is checked on every element of every replica against the oracle, with
+    replica 0 snapshotted on the compute stream before each hook."""
+    L, d, f, T, cap = 24, 2048, 8192, 8192, WC.MLP_OVERLAP.cap_bytes
+    params = WS.mlp(L, d, f)
+    numels = WS.numels(params)
+    P, R = len(numels), 8
+    perm = WG.permutation(55, P)                 # definition index k holds layer-order variable perm[k]
+    dpos = [0] * P
+    for k, v in enumerate(perm):
+        dpos[v] = k
+    say(f"config5 shuffled + rebuild: P={P} R={R}")
+    comp, sides = _bench_streams()
+    with torch.cuda.stream(comp):
+        grads = alloc_grads(numels, R)           # layer-order variables
+        snap = [torch.empty(n, dtype=torch.float32, device="cuda") for n in numels]
+        g = torch.Generator(device="cuda").manual_seed(5)
+        bf = torch.bfloat16
+        X = [torch.randn(T, d, device="cuda", dtype=bf, generator=g) for _ in range(L)]
+        H = [torch.randn(T, f, device="cuda", dtype=bf, generator=g) for _ in range(L)]
+        W1 = [torch.randn(f, d, device="cuda", dtype=bf, generator=g) * 0.02 for _ in range(L)]
+        W2 = [torch.randn(d, f, device="cuda", dtype=bf, generator=g) * 0.02 for _ in range(L)]
+        dY0 = torch.randn(T, d, device="cuda", dtype=bf, generator=g)
+        shapes_def = [params[v].shape for v in perm]
+        grads_def = [[row[v] for v in perm] for row in grads]
+        red = D.Reducer(shapes_def, R, 1 << 62)
+        red.bind(grads_def, compute_stream=comp, side_streams=sides, flags=D.BIND_TIME_LAUNCHES | D.BIND_OVERLAP)
+        g0 = [grads[0][v].view(params[v].shape) for v in range(P)]
+
+        def fill_peers():
+            for r in range(1, R):
+                for v, n in enumerate(numels):
+                    WG.normal(WG.seed_of(5, r, v), n, "cuda", out=grads[r][v])
+
+        fill_peers()
+        _mlp_backward(g0, X, H, W1, W2, dY0, lambda v: red.mark_ready(dpos[v]))
+        red.finalize()
+        assert red.num_buckets == 1
+        red.rebuild_buckets(cap)
+        red.bind(grads_def, compute_stream=comp, side_streams=sides, flags=D.BIND_TIME_LAUNCHES | D.BIND_OVERLAP)
+        fill_peers()                             # the first iteration averaged them
+
+        def hook(v):
+            snap[v].copy_(grads[0][v])
+            red.mark_ready(dpos[v])
+
+        _mlp_backward(g0, X, H, W1, W2, dY0, hook)
+        red.finalize()
+    torch.cuda.synchronize()
+    hook_order = [dpos[v] for v in range(P)][::-1]     # definition indices in the backward's order
+    want_buckets = OP.compute_bucket_assignment_by_size([numels[v] for v in perm], 4, cap, order=hook_order)
+    assert red.buckets() == want_buckets and red.num_buckets == 48
+    assert red.launch_log() == closed_form_launch_log(want_buckets, hook_order)
+    stage = HostStage(R, max(numels))
+    out = np.empty(max(numels), np.float32)
+    with ThreadPoolExecutor(host_workers()) as pool:
+        for v, n in enumerate(numels):
+            _progress(v, P, "rebuilt config5 oracle")
+            bufs = [stage.fetch(0, snap[v])] + [stage.fetch(r, _regen_dev(5, r, v, n)) for r in range(1, R)]
+            want = to_device_f32(_oracle_mean(pool, bufs, out[:n]))
+            for r in range(R):
+                assert_device_bits_equal(grads[r][v], want, f"rebuilt v={v} r={r}")
+    red.close()
