@@ -45,7 +45,7 @@ def _host_inputs(seed, numels, R, kind="normal"):
 RAGGED = [1, 3, 4, 5, 63, 64, 65, 255, 1000, 4095, 4096, 4097, 8191, 8193, 12345, 20000, 2, 777]
 
 
-@pytest.mark.parametrize("R", [1, 2, 3, 5, 8, 16, 17, 33, 64])
+@pytest.mark.parametrize("R", [1, 2, 3, 5, 8, 16, 17, 20, 24, 33, 64])
 @pytest.mark.parametrize("mode", [D.MODE_FUSED, D.MODE_STAGED])
 def test_ragged_parity(R, mode):
     numels = RAGGED
@@ -113,7 +113,7 @@ def test_special_values():
     assert np.array_equal(snapshot(grads)[0][0].view(np.uint32), np.ones(8, np.uint32))
 
 
-@pytest.mark.parametrize("R", [4, 20])
+@pytest.mark.parametrize("R", [4, 20, 24])
 def test_unaligned_views_take_the_scalar_path(R):
     numels = [5, 4096, 37, 1000]
     base = [torch.zeros(sum(numels) + 16, device="cuda") for _ in range(R)]
@@ -403,7 +403,7 @@ def test_capped_grid_parity(mode, blocks):
             assert_bits_equal(got[v][r], want[r][v], f"blocks={blocks} v={v} r={r}")
 
 
-@pytest.mark.parametrize("R", [8, 20])
+@pytest.mark.parametrize("R", [8, 20, 24])
 @pytest.mark.parametrize("wg", [0, 1, 2])
 @pytest.mark.parametrize("flags", [False, True])
 @pytest.mark.parametrize("mode", [D.MODE_FUSED, D.MODE_STAGED])

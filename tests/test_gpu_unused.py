@@ -37,7 +37,7 @@ def _flags(seed, R, P):
     return used
 
 
-@pytest.mark.parametrize("R", [2, 3, 8, 20, 64])
+@pytest.mark.parametrize("R", [2, 3, 8, 20, 24, 64])
 @pytest.mark.parametrize("mode", [D.MODE_FUSED, D.MODE_STAGED])
 def test_unused_parity_copy_modes(R, mode):
     P = len(NUMELS)
