@@ -222,6 +222,67 @@ def test_stream_ordering_with_delayed_producer():
             assert_bits_equal(got[v][r], want[r][v], f"v={v} r={r}")
 
 
+def _delay(stream, n=40):
+    """Queue about 40 dependent fp32 GEMMs (milliseconds of work) on `stream`."""
+    with torch.cuda.stream(stream):
+        a = torch.randn(2048, 2048, device="cuda")
+        for _ in range(n):
+            a = torch.tanh(a @ a * 1e-3)
+    return a
+
+
+@pytest.mark.parametrize("n_side", [1, 2, 3])
+@pytest.mark.parametrize("timed", [False, True])
+@pytest.mark.parametrize("kind", ["fused", "staged", "sync_step"])
+def test_finalize_orders_later_compute_work(kind, timed, n_side):
+    """Work queued on the compute stream after finalize sees the averaged
+    gradients without any host synchronisation ([Li] 3.2: the reduction is
+    done when backward returns). Each side stream is held back by a GEMM chain
+    before the sync, so the device copies queued on the compute stream right
+    after finalize would read unreduced gradients if the join did not order
+    them. Two iterations (the join's events are per iteration); with three
+    side streams and two buckets one stream stays unused."""
+    numels = [4096 * 3 + 5, 999, 50000, 70001, 7]
+    R, P = 4, len(numels)
+    cap = 4 * 60000 if n_side == 3 else 0         # 2 buckets, or one per tensor
+    say(f"join order kind={kind} timed={timed} n_side={n_side}")
+    compute = torch.cuda.Stream()
+    sides = [torch.cuda.Stream() for _ in range(n_side)]
+    red = D.Reducer([(n,) for n in numels], R, cap)
+    grads = alloc_grads(numels, R)
+    mode = D.MODE_STAGED if kind == "staged" else D.MODE_FUSED
+    red.bind(grads, compute_stream=compute, side_streams=sides, mode=mode,
+             flags=D.BIND_TIME_LAUNCHES if timed else 0)
+    order = list(range(P - 1, -1, -1))
+    for it in range(2):
+        host = _host_inputs(41 + it, numels, R)
+        steps_host = _host_inputs(51 + it, numels, R) if kind == "sync_step" else None
+        fill_from_host(grads, host)
+        steps = [[torch.from_numpy(h).cuda() for h in row] for row in steps_host] if steps_host else None
+        torch.cuda.synchronize()
+        keep = [_delay(s) for s in sides]
+        with torch.cuda.stream(compute):
+            if steps is not None:
+                red.set_sync_step(steps)
+            for v in order:
+                red.mark_ready(v)
+            red.finalize()
+            copies = [[g.clone() for g in row] for row in grads]   # queued behind the join only
+        torch.cuda.synchronize()
+        del keep
+        ref = OR.Reducer(numels, R, cap)
+        want = [[np.array(host[r][v], np.float32, copy=True) for v in range(P)] for r in range(R)]
+        ref.bind(want)
+        if steps_host is not None:
+            ref.no_sync_accumulate(steps_host, first=False)
+        ref.sync(order)
+        assert red.launch_log() == ref.launch_log
+        for r in range(R):
+            for v in range(P):
+                assert_bits_equal(copies[r][v].cpu().numpy(), want[r][v], f"it={it} r={r} v={v}")
+    red.close()
+
+
 @pytest.mark.parametrize("layout", ["compute_only", "compute_and_side"])
 def test_compute_stream_as_side_stream(layout):
     """Buckets bound to the compute stream itself run without cross-stream
