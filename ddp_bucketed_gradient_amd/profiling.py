@@ -199,6 +199,29 @@ def overlap_summary(dispatches: List[dict], markers: List[dict], reduction: str,
             "frac_concurrent_with_compute": round(with_comp / total, 4) if total else None}
 
 
+def update_overlap_json(path: str, workload: str, setting: str, summary: dict, profile: str):
+    """Store one phase's overlap figures under `workload` in overlap.json (the
+    file bench.py reads for the --config 5 line), stamped with the hashes of
+    the kernels now built; the other phases of an entry measured with other
+    kernels are dropped."""
+    d = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            d = json.load(f)
+    dev, src = device_code_hash(), kernel_source_hash()
+    e = d.get(workload)
+    if not e or e.get("device_code_sha256_16") != dev:
+        e = {"phases": {}}
+    e.update({"device_code_sha256_16": dev, "kernel_source_sha256_16": src, "profile": profile})
+    e["phases"][setting] = {k: summary[k] for k in ("reduction_launches", "reduction_kernel_ms",
+                                                    "frac_concurrent_with_any_kernel",
+                                                    "frac_concurrent_with_compute")}
+    d[workload] = e
+    with open(path, "w") as f:
+        json.dump(d, f, indent=1, sort_keys=True)
+        f.write("\n")
+
+
 # --- traffic -----------------------------------------------------------------------
 
 def read_counter(run: str, counter: str) -> List[Tuple[str, float]]:
@@ -279,6 +302,10 @@ def main(argv: Optional[Sequence[str]] = None) -> int:
     o.add_argument("--reduction", default="fused_mean_kernel")
     o.add_argument("--phase", required=True, help="regex on the marker range names")
     o.add_argument("--compute", default="Cijk|gemm|Gemm|GEMM", help="regex on the compute kernels' names")
+    o.add_argument("--update", default=None, help="overlap.json to store the phase in")
+    o.add_argument("--key", default=None, help="with --update: the workload's key")
+    o.add_argument("--setting", default=None, help="with --update: the phase's name in the entry")
+    o.add_argument("--profile", default=None, help="with --update: the summary file it comes from")
     c = sub.add_parser("traffic", help="HBM bytes per launch from FETCH_SIZE and WRITE_SIZE runs")
     c.add_argument("--fetch", required=True)
     c.add_argument("--write", required=True)
@@ -292,6 +319,10 @@ def main(argv: Optional[Sequence[str]] = None) -> int:
         out = trace_summary(read_dispatches(a.dir), a.kernel, a.per_sync, a.timed, a.alg_bytes, a.peak)
     elif a.cmd == "overlap":
         out = overlap_summary(read_dispatches(a.dir), read_markers(a.dir), a.reduction, a.phase, a.compute)
+        if a.update:
+            if not (a.key and a.setting and a.profile):
+                ap.error("--update needs --key, --setting and --profile")
+            update_overlap_json(a.update, a.key, a.setting, out, a.profile)
     else:
         out = traffic_summary(read_counter(a.fetch, "FETCH_SIZE"), read_counter(a.write, "WRITE_SIZE"),
                               a.kernel, a.copy_bytes, a.alg_bytes_per_launch)

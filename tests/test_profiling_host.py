@@ -107,3 +107,20 @@ def test_traffic_summary_calibrates_on_copies(tmp_path):
     p = tmp_path / "traffic.json"
     PF.update_traffic_json(str(p), "k:w", out)
     assert json.loads(p.read_text())["k:w"]["bytes_per_launch"] == 51200
+
+
+def test_overlap_json_update_keeps_phases_of_the_same_kernels(tmp_path):
+    p = tmp_path / "overlap.json"
+    ph = {"reduction_launches": 2, "reduction_kernel_ms": 0.2, "frac_concurrent_with_any_kernel": 0.3,
+          "frac_concurrent_with_compute": 0.25, "phase": "x", "windows": 1, "compute_kernels": 1}
+    PF.update_overlap_json(str(p), "w", "wg0", ph, "profiles/x.md")
+    PF.update_overlap_json(str(p), "w", "control", dict(ph, frac_concurrent_with_compute=0.0), "profiles/x.md")
+    e = json.loads(p.read_text())["w"]
+    assert set(e["phases"]) == {"wg0", "control"}
+    assert e["phases"]["control"]["frac_concurrent_with_compute"] == 0.0
+    assert PF.stored_figure_current(e)
+    # an entry measured with other kernels loses its phases at the next update
+    e["device_code_sha256_16"] = "0" * 16
+    p.write_text(json.dumps({"w": e}))
+    PF.update_overlap_json(str(p), "w", "wg1", ph, "profiles/x.md")
+    assert set(json.loads(p.read_text())["w"]["phases"]) == {"wg1"}
