@@ -126,6 +126,37 @@ __device__ __forceinline__ void st4(float* p, v4f v) { *(gv4f*)p = v; }
 __device__ __forceinline__ v4f ld4s(const float* p) { return __builtin_nontemporal_load((const gv4f*)p); }
 __device__ __forceinline__ void st4s(float* p, v4f v) { __builtin_nontemporal_store(v, (gv4f*)p); }
 
+// The reduction kernels address one wavefront's segment of one replica (a
+// wave-uniform base, at most 32 KiB) through a buffer resource, which lets the
+// stores carry device scope (sc1) beside the non-temporal hint: on gfx950 the
+// BERT-large sync (R = 8, cap 25 MiB) ran 1.0 % faster with such stores than
+// with plain non-temporal ones (5,803-5,806 against 5,740-5,749 GB/s, three
+// interleaved runs each on one box; 5,754-5,768 against 5,698-5,706 on
+// another). Device scope without the hint was 3.4 % slower, sc0 with it
+// changed nothing, and none of the policy bits changed anything on the loads,
+// which stay plain non-temporal.
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+constexpr int kPolicyNT = 2;               // cache-policy operand: nt
+constexpr int kPolicyDeviceNT = 2 | 16;    // nt and sc1
+// Word 3 of a gfx9 buffer resource: data format 32 (bits 18:15 = 4), every
+// other field zero (no swizzle, no stride: raw byte offsets, bounded by the
+// record count in bytes; accesses beyond it read zero and write nothing).
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t seg_rsrc(const float* p, int bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  void* base = reinterpret_cast<void*>((static_cast<uintptr_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, kRsrcWord3);
+}
+__device__ __forceinline__ v4f bld4(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kPolicyNT));
+}
+__device__ __forceinline__ void bst4(__amdgpu_buffer_rsrc_t r, int byte_off, v4f v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), r, byte_off, 0, kPolicyDeviceNT);
+}
+
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(1))) v2u gv2u;
 
@@ -204,20 +235,22 @@ __device__ __forceinline__ void zero_fill(float* p, int len, int lane, bool vec)
   if (vec) {
     const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
     const int n4 = len >> 2;
-    for (int i = lane; i < n4; i += 64) st4s(p + 4 * i, zero);
+    const __amdgpu_buffer_rsrc_t rp = seg_rsrc(p, n4 * 16);
+    for (int i = lane; i < n4; i += 64) bst4(rp, 16 * i, zero);
     tail = n4 * 4;
   }
   for (int j = tail + lane; j < len; j += 64) G(p)[j] = 0.0f;
 }
 
-// MASKED = false compiles the used-flag paths out: 168 VGPRs instead of 256
-// VGPRs + 44 AGPRs, so up to three of its waves share a SIMD. Run beside a
-// bf16 GEMM backward with no limit on workgroups per CU it hid 0.16 of the
+// MASKED = false compiles the used-flag paths out: at R = 8, 168 VGPRs instead
+// of 254 VGPRs + 16 AGPRs, so up to three of its waves share a SIMD. Run beside
+// a bf16 GEMM backward with no limit on workgroups per CU it hid 0.16 of the
 // reduction against 0.09-0.11 for one workgroup per CU. The launcher uses it
 // for launches without used flags when workgroups may share CUs
 // (ddpb_set_workgroups_per_cu 0 or 2). At one workgroup per CU the general
-// build streams 0.4 % faster (BERT-large sync: 5,757 vs 5,734 GB/s, three runs
-// each on one box) and is used instead.
+// build streamed 0.4 % faster (BERT-large sync: 5,757 vs 5,734 GB/s, three
+// runs each on one box, both builds with plain non-temporal stores) and is
+// used instead.
 template <int R, bool MASKED>
 __global__ __launch_bounds__(kBlock) void fused_mean_kernel(const Segment* __restrict__ segs, int32_t nseg,
                                                             float* const* __restrict__ grads, int32_t P,
@@ -257,20 +290,23 @@ __global__ __launch_bounds__(kBlock) void fused_mean_kernel(const Segment* __res
       if (vec_ok && (g.flags & kSegVecStart) && (any & 15) == 0) {
         const int n4 = len >> 2;
         const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+        __amdgpu_buffer_rsrc_t rr[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) rr[r] = seg_rsrc(p[r], n4 * 16);
         for (int i = lane; i < n4; i += 64 * UM) {
           v4f x[UM][R];
 #pragma unroll
           for (int u = 0; u < UM; ++u)
 #pragma unroll
             for (int r = 0; r < R; ++r)
-              if (i + 64 * u < n4) x[u][r] = ((mask >> r) & 1u) ? ld4s(p[r] + 4 * (i + 64 * u)) : zero;
+              if (i + 64 * u < n4) x[u][r] = ((mask >> r) & 1u) ? bld4(rr[r], 16 * (i + 64 * u)) : zero;
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int u = 0; u < UM; ++u) {
             if (i + 64 * u < n4) {
               const v4f m = mean4<R>(x[u], scale);
 #pragma unroll
-              for (int r = 0; r < R; ++r) st4s(p[r] + 4 * (i + 64 * u), m);
+              for (int r = 0; r < R; ++r) bst4(rr[r], 16 * (i + 64 * u), m);
             }
           }
         }
@@ -292,6 +328,15 @@ __global__ __launch_bounds__(kBlock) void fused_mean_kernel(const Segment* __res
     int tail = 0;
     if (vec_ok && (g.flags & kSegVecStart) && (any & 15) == 0) {
       const int n4 = len >> 2;
+      // The general build goes through buffer resources (device-scope
+      // stores); the compact build keeps global-pointer accesses with plain
+      // non-temporal stores. Beside the bf16 backward with no per-CU limit the
+      // compact build's buffer form made the step about 1 ms slower (MLP, 24
+      // layers, R = 8: 31.92-32.11 against 30.98-31.06 ms with the global
+      // form, on one box, whether its stores carried device scope or not).
+      __amdgpu_buffer_rsrc_t rr[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) rr[r] = seg_rsrc(p[r], MASKED ? n4 * 16 : 0);
       // Every access of the unrolled group carries its own bound check. The
       // checked loads after the first group then issue one at a time under
       // exec masks instead of back to back; on gfx950 this paced request
@@ -304,7 +349,7 @@ __global__ __launch_bounds__(kBlock) void fused_mean_kernel(const Segment* __res
         for (int u = 0; u < U; ++u)
 #pragma unroll
           for (int r = 0; r < R; ++r)
-            if (i + 64 * u < n4) x[u][r] = ld4s(p[r] + 4 * (i + 64 * u));
+            if (i + 64 * u < n4) x[u][r] = MASKED ? bld4(rr[r], 16 * (i + 64 * u)) : ld4s(p[r] + 4 * (i + 64 * u));
         // Keep all U*R loads in flight: the scheduler may not sink them
         // between the adds (it would otherwise trade bandwidth for registers).
         __builtin_amdgcn_sched_barrier(0);
@@ -313,7 +358,10 @@ __global__ __launch_bounds__(kBlock) void fused_mean_kernel(const Segment* __res
           if (i + 64 * u < n4) {
             const v4f m = mean4<R>(x[u], scale);
 #pragma unroll
-            for (int r = 0; r < R; ++r) st4s(p[r] + 4 * (i + 64 * u), m);
+            for (int r = 0; r < R; ++r) {
+              if constexpr (MASKED) bst4(rr[r], 16 * (i + 64 * u), m);
+              else st4s(p[r] + 4 * (i + 64 * u), m);
+            }
           }
         }
       }
@@ -405,7 +453,7 @@ __global__ __launch_bounds__(kBlock) void fused_mean_kernel_rt(const Segment* __
               m.z = finish_rt(a[u].z, R, scale, pow2 != 0);
               m.w = finish_rt(a[u].w, R, scale, pow2 != 0);
               for (int r = 0; r < R; ++r)
-                st4s(grads[static_cast<int64_t>(r) * P + g.var] + g.start + 4 * (i + 64 * u), m);
+                bst4(seg_rsrc(grads[static_cast<int64_t>(r) * P + g.var] + g.start, n4 * 16), 16 * (i + 64 * u), m);
             }
           }
         }
@@ -558,10 +606,10 @@ __global__ __launch_bounds__(kBlock) void copyback_kernel(const Segment* __restr
           if (i + 64 * u < n4) m[u] = ld4(src + 4 * (i + 64 * u));
         __builtin_amdgcn_sched_barrier(0);
         for (int r = 0; r < R; ++r) {
-          float* dst = grads[static_cast<int64_t>(r) * P + g.var] + g.start;
+          const __amdgpu_buffer_rsrc_t rd = seg_rsrc(grads[static_cast<int64_t>(r) * P + g.var] + g.start, n4 * 16);
 #pragma unroll
           for (int u = 0; u < kCopybackU; ++u)
-            if (i + 64 * u < n4) st4s(dst + 4 * (i + 64 * u), m[u]);
+            if (i + 64 * u < n4) bst4(rd, 16 * (i + 64 * u), m[u]);
         }
       }
       tail = n4 * 4;
@@ -584,7 +632,12 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 
 // Unroll of the accumulation loop and whether it bypasses the caches (each
 // byte is touched once per micro-step; the accumulators of a large model do
-// not stay cached from one micro-step to the next).
+// not stay cached from one micro-step to the next). The add stores with device
+// scope as the reduction does (BERT-base shapes, R = 16, bf16: 2.712-2.714
+// against 2.758-2.761 ms per micro-step, three interleaved runs each); the
+// first micro-step, which only writes, and the synchronising step kept their
+// plain non-temporal stores (device scope: first micro-step 1.712-1.713 against
+// 1.695-1.698 ms, synchronising step no faster).
 constexpr int kAccU = 8;
 // Synchronising step (fused_acc_mean_kernel): replicas per chunk and float4
 // groups per lane in flight. Every load of a chunk issues before its adds:
@@ -629,6 +682,7 @@ __global__ __launch_bounds__(kBlock) void accumulate_kernel(const Segment* __res
     if (vec_ok && (g.flags & kSegVecStart) && (reinterpret_cast<uintptr_t>(acc) & 15) == 0 &&
         (reinterpret_cast<uintptr_t>(st) & 7) == 0) {
       const int n4 = len >> 2;
+      const __amdgpu_buffer_rsrc_t racc = seg_rsrc(acc, n4 * 16);
       for (int i = lane; i < n4; i += 64 * U) {
         v2u b[U];
         v4f a[U];
@@ -654,7 +708,8 @@ __global__ __launch_bounds__(kBlock) void accumulate_kernel(const Segment* __res
               s4.z = a[u].z + s4.z;
               s4.w = a[u].w + s4.w;
             }
-            st4x<kAccNT>(acc + 4 * (i + 64 * u), s4);
+            if (FIRST) st4x<kAccNT>(acc + 4 * (i + 64 * u), s4);
+            else bst4(racc, 16 * (i + 64 * u), s4);
           }
         }
       }
@@ -669,6 +724,7 @@ __global__ __launch_bounds__(kBlock) void accumulate_kernel(const Segment* __res
     if (vec_ok && (g.flags & kSegVecStart) &&
         ((reinterpret_cast<uintptr_t>(acc) | reinterpret_cast<uintptr_t>(st)) & 15) == 0) {
       const int n4 = len >> 2;
+      const __amdgpu_buffer_rsrc_t racc = seg_rsrc(acc, n4 * 16);
       for (int i = lane; i < n4; i += 64 * U) {
         v4f b[U];
         v4f a[U];
@@ -690,7 +746,8 @@ __global__ __launch_bounds__(kBlock) void accumulate_kernel(const Segment* __res
               s4.z = a[u].z + s4.z;
               s4.w = a[u].w + s4.w;
             }
-            st4x<kAccNT>(acc + 4 * (i + 64 * u), s4);
+            if (FIRST) st4x<kAccNT>(acc + 4 * (i + 64 * u), s4);
+            else bst4(racc, 16 * (i + 64 * u), s4);
           }
         }
       }
