@@ -222,6 +222,42 @@ def update_overlap_json(path: str, workload: str, setting: str, summary: dict, p
         f.write("\n")
 
 
+# --- host ranges ---------------------------------------------------------------------
+
+def ranges_summary(dispatches: List[dict], markers: List[dict], kernel: str) -> dict:
+    """The library's roctx ranges (DDPB_BIND_ROCTX) against the device: per
+    range kind, count and average / min / max duration; and for the last
+    sync (from the last `ddpb launch` range that opens a sync, i.e. the
+    first launch after a finalize join, to that sync's join) the host's span,
+    the device span of the kernels those launches issued (the matching
+    dispatches of `kernel`, one per single-bucket launch range, in order) and
+    how long after its range opened each kernel started."""
+    lr = sorted((m for m in markers if m["name"].startswith("ddpb ")), key=lambda m: m["start"])
+    kinds: dict = {}
+    for m in lr:
+        n = m["name"]
+        kind = "launch 0-0" if n == "ddpb launch 0-0" else ("launch b-b" if n.startswith("ddpb launch") else n[5:])
+        kinds.setdefault(kind, []).append((m["end"] - m["start"]) / 1e3)
+    out = {"ranges": {k: {"calls": len(v), "avg_us": round(sum(v) / len(v), 1), "min_us": round(min(v), 1),
+                          "max_us": round(max(v), 1)} for k, v in kinds.items()}}
+    joins = [i for i, m in enumerate(lr) if m["name"] == "ddpb finalize join"]
+    if not joins:
+        return out
+    last = joins[-1]
+    first = joins[-2] + 1 if len(joins) > 1 else 0
+    launches = [m for m in lr[first:last] if m["name"].startswith("ddpb launch")]
+    ks = [d for d in dispatches if re.search(kernel, d["name"]) and d["start"] >= launches[0]["start"]]
+    ks = ks[:len(launches)]
+    if len(ks) < len(launches):
+        return out
+    delays = [(k["start"] - m["start"]) / 1e3 for k, m in zip(ks, launches)]
+    out.update({"last_sync_launch_ranges": len(launches),
+                "last_sync_host_span_us": round((lr[last]["end"] - launches[0]["start"]) / 1e3, 1),
+                "last_sync_device_span_us": round((max(k["end"] for k in ks) - min(k["start"] for k in ks)) / 1e3, 1),
+                "kernel_start_after_range_open_us": [round(min(delays), 1), round(max(delays), 1)]})
+    return out
+
+
 # --- traffic -----------------------------------------------------------------------
 
 def read_counter(run: str, counter: str) -> List[Tuple[str, float]]:
@@ -306,6 +342,9 @@ def main(argv: Optional[Sequence[str]] = None) -> int:
     o.add_argument("--key", default=None, help="with --update: the workload's key")
     o.add_argument("--setting", default=None, help="with --update: the phase's name in the entry")
     o.add_argument("--profile", default=None, help="with --update: the summary file it comes from")
+    g = sub.add_parser("ranges", help="the library's roctx ranges against the kernels they issued")
+    g.add_argument("dir")
+    g.add_argument("--kernel", default="fused_mean_kernel")
     c = sub.add_parser("traffic", help="HBM bytes per launch from FETCH_SIZE and WRITE_SIZE runs")
     c.add_argument("--fetch", required=True)
     c.add_argument("--write", required=True)
@@ -323,6 +362,8 @@ def main(argv: Optional[Sequence[str]] = None) -> int:
             if not (a.key and a.setting and a.profile):
                 ap.error("--update needs --key, --setting and --profile")
             update_overlap_json(a.update, a.key, a.setting, out, a.profile)
+    elif a.cmd == "ranges":
+        out = ranges_summary(read_dispatches(a.dir), read_markers(a.dir), a.kernel)
     else:
         out = traffic_summary(read_counter(a.fetch, "FETCH_SIZE"), read_counter(a.write, "WRITE_SIZE"),
                               a.kernel, a.copy_bytes, a.alg_bytes_per_launch)

@@ -124,3 +124,22 @@ def test_overlap_json_update_keeps_phases_of_the_same_kernels(tmp_path):
     p.write_text(json.dumps({"w": e}))
     PF.update_overlap_json(str(p), "w", "wg1", ph, "profiles/x.md")
     assert set(json.loads(p.read_text())["w"]["phases"]) == {"wg1"}
+
+
+def test_ranges_summary_matches_launch_ranges_to_their_kernels():
+    # two syncs of two single-bucket launches each; kernels start 5 and 7 us after their ranges open
+    mk = lambda n, s, e: {"name": n, "start": s, "end": e}  # noqa: E731
+    markers = [mk("ddpb launch 0-0", 0, 40_000), mk("ddpb launch 1-1", 50_000, 80_000),
+               mk("ddpb finalize join", 90_000, 100_000),
+               mk("ddpb launch 0-0", 200_000, 230_000), mk("ddpb launch 1-1", 240_000, 260_000),
+               mk("ddpb finalize join", 270_000, 290_000), mk("bench other", 0, 1)]
+    disp = [{"name": "fused_mean_kernel<8, true>", "id": i, "start": s, "end": s + 300_000}
+            for i, s in enumerate([5_000, 57_000, 205_000, 247_000])]
+    disp.append({"name": "other", "id": 9, "start": 201_000, "end": 202_000})
+    out = PF.ranges_summary(disp, markers, "fused_mean_kernel")
+    assert out["ranges"]["launch 0-0"] == {"calls": 2, "avg_us": 35.0, "min_us": 30.0, "max_us": 40.0}
+    assert out["ranges"]["launch b-b"]["calls"] == 2 and out["ranges"]["finalize join"]["avg_us"] == 15.0
+    assert out["last_sync_launch_ranges"] == 2
+    assert out["last_sync_host_span_us"] == 90.0
+    assert out["last_sync_device_span_us"] == 342.0
+    assert out["kernel_start_after_range_open_us"] == [5.0, 7.0]
