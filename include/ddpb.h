@@ -150,7 +150,9 @@ int ddpb_workspace_bytes(ddpb_t h, int32_t mode, int64_t* bytes);
  *                  itself: its buckets then run in order with the compute
  *                  work, with no cross-stream events (nothing overlaps them;
  *                  the lowest latency when there is no backward to hide
- *                  behind).
+ *                  behind). A plan of a single bucket always reduces on the
+ *                  compute stream: that bucket launches only once the last
+ *                  gradient is ready, so there is nothing to overlap.
  *   mode, flags    DDPB_MODE_*, DDPB_BIND_*.
  * Synchronizes the compute stream once to upload the tables. Not allowed
  * while an iteration is in progress. */
