@@ -15,7 +15,10 @@
 // v4fs at lane stride, so one instruction covers 1 KiB of contiguous memory
 // per replica. An unrolled group issues all of its R x U loads before the
 // first add, to keep enough bytes in flight, each under its own bound check
-// so that they leave one at a time (measured faster than back to back).
+// so that they leave one at a time (measured faster than back to back). All
+// gradient streams are non-temporal; the reduction's stores (and those of the
+// bf16 accumulation and the staged copy-back) also carry device scope, which
+// needs the buffer-resource form of the accesses (seg_rsrc below).
 //
 // Kernels
 //   fused_mean_kernel   gather (pack), R-way mean and copy-back in one pass:
@@ -27,6 +30,8 @@
 //                       grid-stride over contiguous v4fs.
 //   copyback_kernel     staged step 3: averaged bucket -> R gradients.
 //   accumulate_kernel   no_sync: grad (+)= float(step) for every replica.
+//   fused_acc_mean_kernel  the synchronising micro-step fused into the
+//                       reduction: mean of (grad + float(step)) in one pass.
 //
 // With used flags (unused parameters) the kernels read zeros for replicas that
 // did not use a variable and skip variables no replica used (bucket views:
