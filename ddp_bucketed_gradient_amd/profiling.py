@@ -30,7 +30,7 @@ import json
 import os
 import re
 import sys
-from typing import Dict, List, Optional, Sequence, Tuple
+from typing import List, Optional, Sequence, Tuple
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))

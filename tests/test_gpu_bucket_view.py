@@ -6,9 +6,9 @@ import pytest
 import torch
 
 import ddp_bucketed_gradient_amd as D
-from gpu_util import require_gpu, say, assert_bits_equal
+from gpu_util import require_gpu, assert_bits_equal
 from oracle import reducer as OR
-from workloads import gen as WG, configs as WC
+from workloads import gen as WG
 
 pytestmark = pytest.mark.gpu
 

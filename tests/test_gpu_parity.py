@@ -14,7 +14,7 @@ import ddp_bucketed_gradient_amd as D
 from gpu_util import require_gpu, say, alloc_grads, fill_from_host, snapshot, assert_bits_equal
 from oracle import reducer as OR
 from oracle import linear10 as OL
-from workloads import shapes as WS, gen as WG, configs as WC
+from workloads import gen as WG, configs as WC
 
 pytestmark = pytest.mark.gpu
 MiB = 1 << 20

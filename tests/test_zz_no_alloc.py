@@ -2,7 +2,6 @@
 oracle: the same bits, 0 ULP, every element of every replica, on two calls in
 a row (the second with a smaller model that takes the static array over), in
 fused and staged modes; a model too large for the array is refused."""
-import numpy as np
 import pytest
 import torch
 
