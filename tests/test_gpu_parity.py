@@ -283,6 +283,41 @@ def test_finalize_orders_later_compute_work(kind, timed, n_side):
     red.close()
 
 
+def test_single_bucket_reduces_on_the_compute_stream():
+    """A plan of one bucket reduces on the compute stream whatever side
+    streams are bound: with both side streams held back by GEMM chains, the
+    synchronised gradients are on the compute stream (and bit-exact) while the
+    side streams are still busy, so nothing waited for them."""
+    numels = [4096 * 3 + 5, 999, 7]
+    R, P = 4, len(numels)
+    compute = torch.cuda.Stream()
+    sides = [torch.cuda.Stream() for _ in range(2)]
+    red = D.Reducer([(n,) for n in numels], R, 1 << 30)
+    assert red.num_buckets == 1
+    grads = alloc_grads(numels, R)
+    red.bind(grads, compute_stream=compute, side_streams=sides)
+    host = _host_inputs(61, numels, R)
+    fill_from_host(grads, host)
+    torch.cuda.synchronize()
+    keep = [_delay(s, 200) for s in sides]
+    with torch.cuda.stream(compute):
+        red.sync(list(range(P - 1, -1, -1)))
+        copies = [[g.clone() for g in row] for row in grads]
+        done = torch.cuda.Event()
+        done.record(compute)
+    done.synchronize()
+    busy = [not s.query() for s in sides]
+    torch.cuda.synchronize()
+    del keep
+    assert all(busy), "the single bucket waited for the side streams"
+    want, log = _oracle_sync(numels, R, 1 << 30, host, list(range(P - 1, -1, -1)))
+    assert red.launch_log() == log
+    for r in range(R):
+        for v in range(P):
+            assert_bits_equal(copies[r][v].cpu().numpy(), want[r][v], f"r={r} v={v}")
+    red.close()
+
+
 @pytest.mark.parametrize("layout", ["compute_only", "compute_and_side"])
 def test_compute_stream_as_side_stream(layout):
     """Buckets bound to the compute stream itself run without cross-stream
