@@ -270,6 +270,15 @@ def read_counter(run: str, counter: str) -> List[Tuple[str, float]]:
     return out
 
 
+def counter_summary(rows: List[Tuple[str, float]], kernel: str) -> dict:
+    """Sum and per-dispatch mean of one counter over the dispatches of the
+    kernels whose name matches `kernel`."""
+    vals = [v for name, v in rows if re.search(kernel, name)]
+    if not vals:
+        raise ValueError(f"no dispatch of {kernel!r} in the counter run")
+    return {"dispatches": len(vals), "total": sum(vals), "per_dispatch": round(sum(vals) / len(vals), 1)}
+
+
 def traffic_summary(fetch: List[Tuple[str, float]], write: List[Tuple[str, float]], kernel: str,
                     copy_bytes: float, alg_bytes_per_launch: float, copy_kernel: str = "copyBuffer") -> dict:
     """HBM bytes per launch of `kernel` from the FETCH_SIZE and WRITE_SIZE
@@ -345,6 +354,10 @@ def main(argv: Optional[Sequence[str]] = None) -> int:
     g = sub.add_parser("ranges", help="the library's roctx ranges against the kernels they issued")
     g.add_argument("dir")
     g.add_argument("--kernel", default="fused_mean_kernel")
+    n = sub.add_parser("counters", help="totals of counters over a kernel's dispatches in a --pmc run")
+    n.add_argument("dir")
+    n.add_argument("--counter", action="append", required=True, help="counter name as in the CSV (repeatable)")
+    n.add_argument("--kernel", required=True, help="regex on the kernel name")
     c = sub.add_parser("traffic", help="HBM bytes per launch from FETCH_SIZE and WRITE_SIZE runs")
     c.add_argument("--fetch", required=True)
     c.add_argument("--write", required=True)
@@ -362,6 +375,8 @@ def main(argv: Optional[Sequence[str]] = None) -> int:
             if not (a.key and a.setting and a.profile):
                 ap.error("--update needs --key, --setting and --profile")
             update_overlap_json(a.update, a.key, a.setting, out, a.profile)
+    elif a.cmd == "counters":
+        out = {name: counter_summary(read_counter(a.dir, name), a.kernel) for name in a.counter}
     elif a.cmd == "ranges":
         out = ranges_summary(read_dispatches(a.dir), read_markers(a.dir), a.kernel)
     else:

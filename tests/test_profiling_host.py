@@ -143,3 +143,18 @@ def test_ranges_summary_matches_launch_ranges_to_their_kernels():
     assert out["last_sync_host_span_us"] == 90.0
     assert out["last_sync_device_span_us"] == 342.0
     assert out["kernel_start_after_range_open_us"] == [5.0, 7.0]
+
+
+def test_counter_summary_sums_a_kernels_dispatches(tmp_path):
+    with open(tmp_path / "r_counter_collection.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writerow([1, "copyBuffer", "TCC_EA0_WRREQ_sum", 7.0])
+        w.writerow([2, "fused_mean_kernel<8, true>", "TCC_EA0_WRREQ_sum", 10.0])
+        w.writerow([2, "fused_mean_kernel<8, true>", "TCC_EA0_WRREQ_64B_sum", 4.0])
+        w.writerow([3, "fused_mean_kernel<8, true>", "TCC_EA0_WRREQ_sum", 20.0])
+    rows = PF.read_counter(str(tmp_path), "TCC_EA0_WRREQ_sum")
+    assert PF.counter_summary(rows, "fused_mean") == {"dispatches": 2, "total": 30.0, "per_dispatch": 15.0}
+    assert PF.counter_summary(PF.read_counter(str(tmp_path), "TCC_EA0_WRREQ_64B_sum"), "fused")["total"] == 4.0
+    with pytest.raises(ValueError):
+        PF.counter_summary(rows, "accumulate")
